@@ -1,0 +1,291 @@
+"""Thin ctypes binding of the C-ABI attention library (libattn.so).
+
+Argument marshalling only: torch tensors provide device memory and the
+current stream; every step of the computation runs in the library's HIP
+kernels.  Importing this module loads the library and raises ImportError
+when it has not been built (there is no fallback path).
+
+Function names mirror include/attn.h: attn_fwd, attn_bwd, attn_decode,
+block_mask_build.  Tensors use the logical layout [B, S, H, D] of
+flash_attn_func (q [B, Sq, Hq, D], k / v [B, Sk, Hkv, D]); any strides
+with a unit head-dim stride and 16-byte aligned rows are passed through
+without copies.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        "libattn.so is not built; run `python -m exact_attention_10_amd.build` "
+        "(or __graft_entry__.build()) first")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+ATTN_OK = 0
+ATTN_BF16 = 0
+ATTN_FP32 = 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
+          3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+class attn_tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("stride", ctypes.c_int64 * 4)]
+
+
+class attn_mask_desc(ctypes.Structure):
+    _fields_ = [("causal", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32), ("doc_q", ctypes.c_void_p),
+                ("doc_k", ctypes.c_void_p)]
+
+
+class attn_block_mask(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("nQ", ctypes.c_int32), ("nK", ctypes.c_int32),
+                ("desc", attn_mask_desc),
+                ("cls", ctypes.c_void_p),
+                ("kv_num_partial", ctypes.c_void_p), ("kv_idx_partial", ctypes.c_void_p),
+                ("kv_num_full", ctypes.c_void_p), ("kv_idx_full", ctypes.c_void_p),
+                ("q_num_partial", ctypes.c_void_p), ("q_idx_partial", ctypes.c_void_p),
+                ("q_num_full", ctypes.c_void_p), ("q_idx_full", ctypes.c_void_p)]
+
+
+class attn_params(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Sq", ctypes.c_int32), ("Sk", ctypes.c_int32),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+                ("alibi_slopes", ctypes.c_void_p), ("alibi_batch_stride", ctypes.c_int64),
+                ("softcap", ctypes.c_float),
+                ("block_mask", ctypes.POINTER(attn_block_mask))]
+
+
+_P = ctypes.POINTER
+_lib.attn_status_string.restype = ctypes.c_char_p
+_lib.attn_status_string.argtypes = [ctypes.c_int]
+_lib.attn_last_error.restype = ctypes.c_char_p
+_lib.attn_last_error.argtypes = []
+_lib.attn_fwd.restype = ctypes.c_int
+_lib.attn_fwd.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor, attn_tensor,
+                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                          ctypes.c_void_p]
+_lib.attn_fwd_tile_shape.restype = ctypes.c_int
+_lib.attn_fwd_tile_shape.argtypes = [_P(attn_params), ctypes.c_int32, _P(ctypes.c_int32),
+                                     _P(ctypes.c_int32)]
+_lib.attn_bwd.restype = ctypes.c_int
+_lib.attn_bwd.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor, attn_tensor,
+                          attn_tensor, ctypes.c_void_p, attn_tensor, attn_tensor, attn_tensor,
+                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+_lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+_lib.attn_bwd_workspace_size.argtypes = [_P(attn_params)]
+_lib.attn_decode.restype = ctypes.c_int
+_lib.attn_decode.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor,
+                             ctypes.c_void_p, ctypes.c_int32, attn_tensor, ctypes.c_void_p,
+                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+_lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+_lib.attn_decode_workspace_size.argtypes = [_P(attn_params), ctypes.c_int32]
+_lib.attn_block_mask_bytes.restype = ctypes.c_size_t
+_lib.attn_block_mask_bytes.argtypes = [ctypes.c_int32] * 5
+_lib.block_mask_build.restype = ctypes.c_int
+_lib.block_mask_build.argtypes = [_P(attn_mask_desc), ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_size_t, _P(attn_block_mask),
+                                  ctypes.c_void_p]
+
+EXPORTED = ["attn_status_string", "attn_last_error", "attn_fwd", "attn_fwd_tile_shape",
+            "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+            "attn_decode_workspace_size", "attn_block_mask_bytes", "block_mask_build"]
+
+
+def library():
+    return _lib
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, _lib.attn_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_FP32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _tensor(t):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-d [B, S, H, D] tensor, got shape %s" % (tuple(t.shape),))
+    s = attn_tensor()
+    s.data = t.data_ptr()
+    s.dtype = _dtype_code(t)
+    for i in range(4):
+        s.stride[i] = t.stride(i)
+    return s
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class BlockMask:
+    """Device block mask built by block_mask_build (keeps its buffer alive)."""
+
+    def __init__(self, struct, buffer, doc_q, doc_k):
+        self.struct = struct
+        self.buffer = buffer
+        self._docs = (doc_q, doc_k)
+
+    def _view(self, field, dtype, shape):
+        ptr = getattr(self.struct, field)
+        off = ptr - self.buffer.data_ptr()
+        n = 1
+        for x in shape:
+            n *= x
+        size = torch.empty((), dtype=dtype).element_size()
+        return self.buffer[off:off + n * size].view(dtype).view(*shape)
+
+    def arrays(self):
+        s = self.struct
+        B, nQ, nK = s.B, s.nQ, s.nK
+        return {
+            "cls": self._view("cls", torch.uint8, (B, nQ, nK)),
+            "kv_num_partial": self._view("kv_num_partial", torch.int32, (B, nQ)),
+            "kv_idx_partial": self._view("kv_idx_partial", torch.int32, (B, nQ, nK)),
+            "kv_num_full": self._view("kv_num_full", torch.int32, (B, nQ)),
+            "kv_idx_full": self._view("kv_idx_full", torch.int32, (B, nQ, nK)),
+            "q_num_partial": self._view("q_num_partial", torch.int32, (B, nK)),
+            "q_idx_partial": self._view("q_idx_partial", torch.int32, (B, nK, nQ)),
+            "q_num_full": self._view("q_num_full", torch.int32, (B, nK)),
+            "q_idx_full": self._view("q_idx_full", torch.int32, (B, nK, nQ)),
+        }
+
+
+def block_mask_build(B, Sq, Sk, block_m=128, block_n=128, causal=False, window=(-1, -1),
+                     doc_q=None, doc_k=None, device="cuda"):
+    """Build a block mask on the device (doc_q / doc_k: int32 [B, S] device tensors)."""
+    desc = attn_mask_desc()
+    desc.causal = int(bool(causal))
+    desc.window_left, desc.window_right = int(window[0]), int(window[1])
+    if doc_q is not None:
+        doc_q = doc_q.contiguous()
+        doc_k = doc_k.contiguous()
+        assert doc_q.dtype == torch.int32 and doc_k.dtype == torch.int32
+    desc.doc_q = None if doc_q is None else doc_q.data_ptr()
+    desc.doc_k = None if doc_k is None else doc_k.data_ptr()
+    nbytes = _lib.attn_block_mask_bytes(B, Sq, Sk, block_m, block_n)
+    buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    out = attn_block_mask()
+    _check(_lib.block_mask_build(ctypes.byref(desc), B, Sq, Sk, block_m, block_n,
+                                 ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.byref(out),
+                                 _stream()))
+    return BlockMask(out, buf, doc_q, doc_k)
+
+
+def _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask):
+    p = attn_params()
+    p.B, p.Sq, p.Hq = q.shape[0], q.shape[1], q.shape[2]
+    p.Sk, p.Hkv = k.shape[1], k.shape[2]
+    p.D = D
+    p.softmax_scale = math.nan if softmax_scale is None else float(softmax_scale)
+    p.causal = int(bool(causal))
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous float32 tensor")
+        p.alibi_slopes = alibi_slopes.data_ptr()
+        p.alibi_batch_stride = 0 if alibi_slopes.dim() == 1 else alibi_slopes.shape[-1]
+    else:
+        p.alibi_slopes = None
+        p.alibi_batch_stride = 0
+    p.softcap = float(softcap)
+    p.block_mask = ctypes.pointer(block_mask.struct) if block_mask is not None else None
+    return p
+
+
+def tile_shape(q, k, block_mask=None):
+    p = _params(q, k, q.shape[3], None, False, (-1, -1), None, 0.0, block_mask)
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.attn_fwd_tile_shape(ctypes.byref(p), _dtype_code(q), ctypes.byref(bm),
+                                    ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def attn_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), alibi_slopes=None,
+             softcap=0.0, block_mask=None, out=None, lse=None, tile_trace=None):
+    """Forward attention.  Returns (out [B, Sq, Hq, D], lse fp32 [B, Hq, Sq])."""
+    B, Sq, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask)
+    _check(_lib.attn_fwd(ctypes.byref(p), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
+                         _ptr(lse), _ptr(tile_trace), None, 0, _stream()))
+    return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, window=(-1, -1),
+             alibi_slopes=None, softcap=0.0, deterministic=True, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Backward attention from the saved LSE.  Returns (dq, dk, dv)."""
+    D = q.shape[3]
+    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, None)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = _lib.attn_bwd_workspace_size(ctypes.byref(p))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.attn_bwd(ctypes.byref(p), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
+                         _tensor(dout), _ptr(lse), _tensor(dq), _tensor(dk), _tensor(dv),
+                         1 if deterministic else 0, _ptr(workspace), workspace.numel(),
+                         _stream()))
+    return dq, dk, dv
+
+
+def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=0.0,
+                num_splits=0, out=None, lse=None, workspace=None):
+    """Decode over a KV cache.  q [B, 1, Hq, D]; caches [B, Smax, Hkv, D];
+    cache_seqlens int32 [B] on the device.  Returns (out, lse [B, Hq, 1])."""
+    B, Sq, Hq, D = q.shape
+    p = _params(q, k_cache, D, softmax_scale, False, (-1, -1), None, softcap, None)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32")
+    need = _lib.attn_decode_workspace_size(ctypes.byref(p), int(num_splits))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.attn_decode(ctypes.byref(p), _tensor(q), _tensor(k_cache), _tensor(v_cache),
+                            _ptr(cache_seqlens), int(num_splits), _tensor(out), _ptr(lse),
+                            _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse
+
+
+def decode_workspace_size(q, k_cache, num_splits=0, softcap=0.0):
+    p = _params(q, k_cache, q.shape[3], None, False, (-1, -1), None, softcap, None)
+    return _lib.attn_decode_workspace_size(ctypes.byref(p), int(num_splits))
+
+
+def bwd_workspace_size(q, k):
+    p = _params(q, k, q.shape[3], None, False, (-1, -1), None, 0.0, None)
+    return _lib.attn_bwd_workspace_size(ctypes.byref(p))

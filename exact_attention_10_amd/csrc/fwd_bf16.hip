@@ -1,0 +1,393 @@
+// Forward attention, bf16 inputs, MFMA (gfx950).
+//
+// Tiled exact attention with an online softmax ("Accelerating AI: A Deep
+// Dive into Flash Attention", sections "Tiling the Computation",
+// "2. Online Softmax" and "3. Weighted Sum of Values"): each workgroup owns
+// 128 query rows of one (batch, query head), streams 64-key tiles of the
+// matching key/value head through LDS, and keeps a running row maximum, row
+// sum and unnormalised output in registers, so scores never reach HBM.
+//
+// Work split.  4 waves x 32 query rows.  Each wave computes the transposed
+// score tile S^T = K Q^T (64 keys x 32 queries) with 32x32x16 MFMAs: K comes
+// from LDS (A operand), the wave's Q rows stay in registers (B operand) for
+// the whole key loop.  In the S^T accumulator a lane holds 16 keys of one
+// query per 32-key half, so the row statistics are in-lane reductions plus
+// one exchange with lane l^32.  The same accumulator registers, rounded to
+// bf16, are exactly the B operand of O^T += V^T P^T; V^T comes from LDS via
+// transposed reads (ds_read_b64_tr_b16), so P never leaves registers.
+//
+// Score modifiers and masks are the FlexAttention hooks of "Lightning Talk:
+// FlexAttention + FlashAttention-4" (score_mod: ALiBi, tanh softcap;
+// mask_mod: causal, sliding window, document) and flash_attn_func's
+// causal / window_size / alibi_slopes / softcap arguments ("FlashAttention:
+// Fast and Memory-Efficient Exact Attention", "Examples").  Masks are
+// evaluated only on PARTIAL tiles; EMPTY tiles are never visited.
+//
+// The running maximum is rescaled lazily: the output and sum are only
+// rescaled when a row's maximum grows by more than 2^8 (in exp2 units) over
+// the maximum in use, so p = exp2(x - m_used) <= 256.  Sum and output use the
+// same m_used, so the final O = acc / l and LSE = m_used + log2(l) are exact.
+
+#include "common.h"
+#include "internal.h"
+
+namespace attn {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BM = kFwdBM;        // query rows per workgroup
+  static constexpr int BN = kFwdBN;        // keys per tile
+  static constexpr int NT = 256;           // threads (4 waves)
+  static constexpr int KS = D + 8;         // K row stride in LDS (elements)
+  static constexpr int VS = D + 32;        // V row stride in LDS (elements)
+  static constexpr int KT = BN * KS;       // elements per K buffer
+  static constexpr int VT = BN * VS;       // elements per V buffer
+  static constexpr int CPT = BN * D / 8 / NT;  // 16-byte chunks per thread
+  static constexpr int DSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+};
+
+struct Tile {
+  int kt;
+  bool full;
+};
+
+__device__ __forceinline__ bf16x8 zero_frag() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+}
+
+template <int D, int MOD>  // MOD bit 0: ALiBi, bit 1: softcap
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  constexpr bool kAlibi = MOD & 1;
+  constexpr bool kSoftcap = MOD & 2;
+
+  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * C::KT];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * C::VT];
+  __shared__ int lds_doc[2 * C::BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;   // k-group of the MFMA operands
+  const int c = lane & 31;   // column (query) of S^T / O^T
+
+  // Heaviest query tiles first (causal work grows with the tile index); the
+  // head index is permuted so that consecutive workgroups, which the
+  // dispatcher places on different XCDs, keep one GQA group per XCD.
+  const int nqt = (a.Sq + C::BM - 1) / C::BM;
+  const int per_qt = a.Hq * a.B;
+  const int bid = blockIdx.x;
+  const int qt = nqt - 1 - bid / per_qt;
+  const int rem = bid % per_qt;
+  const int b = rem / a.Hq;
+  int h = rem % a.Hq;
+  if ((a.Hq & 7) == 0) h = (h & 7) * (a.Hq >> 3) + (h >> 3);
+  const int G = a.Hq / a.Hkv;
+  const int kvh = h / G;
+
+  const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.k_sb + kvh * a.k_sh;
+  const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.v_sb + kvh * a.v_sh;
+
+  const int my_q = qt * C::BM + wave * 32 + c;
+  const bool q_ok = my_q < a.Sq;
+
+  // Q fragments (B operand): column my_q, d = 16*ds + 8*g .. +7.  A negative
+  // scale is folded into Q by an exact sign flip so the exponent scale is
+  // positive and row maxima can be taken on the raw dot products.
+  const float scale_abs = fabsf(a.scale);
+  const uint32_t sign_flip = a.scale < 0.0f ? 0x80008000u : 0u;
+  bf16x8 qf[C::DSTEPS];
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    if (q_ok) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qp + (int64_t)my_q * a.q_ss + 16 * ds + 8 * g);
+      raw.x ^= sign_flip; raw.y ^= sign_flip; raw.z ^= sign_flip; raw.w ^= sign_flip;
+      qf[ds] = __builtin_bit_cast(bf16x8, raw);
+    } else {
+      qf[ds] = zero_frag();
+    }
+  }
+
+  const float scale_log2 = scale_abs * kLog2e;
+  float slope_log2 = 0.0f;
+  if (kAlibi) slope_log2 = a.alibi[b * a.alibi_sb + h] * kLog2e;
+  const float cap = a.softcap;
+  const float cap_k2 = kSoftcap ? 2.0f * kLog2e * scale_abs / cap : 0.0f;
+  const float cap_log2 = cap * kLog2e;
+
+  // Tile schedule: dense (causal / window interval) or block-mask lists.
+  const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
+  const TileRange range(win, qt, C::BM, C::BN);
+  const bool sparse = a.tiles.kv_num_full != nullptr;
+  int n_full = 0, ntiles;
+  const int32_t* idx_full = nullptr;
+  const int32_t* idx_part = nullptr;
+  if (sparse) {
+    const int row = b * a.tiles.nQ + qt;
+    n_full = a.tiles.kv_num_full[row];
+    const int n_part = a.tiles.kv_num_partial[row];
+    idx_full = a.tiles.kv_idx_full + (int64_t)row * a.tiles.nK;
+    idx_part = a.tiles.kv_idx_partial + (int64_t)row * a.tiles.nK;
+    ntiles = (n_full + n_part) * a.tiles.sub;
+  } else {
+    ntiles = range.kt_end - range.kt_begin;
+  }
+  auto tile_at = [&](int t) -> Tile {
+    Tile r;
+    if (!sparse) {
+      r.kt = range.kt_begin + t;
+      r.full = range.full(win, r.kt, C::BM, C::BN);
+    } else {
+      const int mt = t / a.tiles.sub, sb = t % a.tiles.sub;
+      if (mt < n_full) {
+        r.kt = idx_full[mt] * a.tiles.sub + sb;
+        r.full = true;
+      } else {
+        r.kt = idx_part[mt - n_full] * a.tiles.sub + sb;
+        r.full = false;
+      }
+    }
+    return r;
+  };
+
+  const bool has_doc = a.mask.doc_q != nullptr;
+  const int doc_mine = (has_doc && q_ok) ? a.mask.doc_q[(int64_t)b * a.Sq + my_q] : 0;
+  const int delta = a.Sk - a.Sq;
+
+  uint4 kr[C::CPT], vr[C::CPT];
+  int doc_r = 0;
+  auto load_regs = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int chunk = tid + u * C::NT;
+      const int row = chunk / (D / 8);
+      const int col = (chunk % (D / 8)) * 8;
+      const int key = kt * C::BN + row;
+      if (key < a.Sk) {
+        kr[u] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * a.k_ss + col);
+        vr[u] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * a.v_ss + col);
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (has_doc && tid < C::BN) {
+      const int key = kt * C::BN + tid;
+      doc_r = key < a.Sk ? a.mask.doc_k[(int64_t)b * a.Sk + key] : -1;
+    }
+  };
+  auto store_regs = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int chunk = tid + u * C::NT;
+      const int row = chunk / (D / 8);
+      const int col = (chunk % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(lds_k + buf * C::KT + row * C::KS + col) = kr[u];
+      *reinterpret_cast<uint4*>(lds_v + buf * C::VT + row * C::VS + col) = vr[u];
+    }
+    if (has_doc && tid < C::BN) lds_doc[buf * C::BN + tid] = doc_r;
+  };
+
+  uint8_t* trace_row = nullptr;
+  if (a.trace != nullptr && tid == 0)
+    trace_row = a.trace + ((int64_t)(b * a.Hq + h) * a.nQt + qt) * a.nKt;
+
+  float m_run = kNegInf;  // running max (exp2 domain), shared by lanes c, c+32
+  float l_run = 0.0f;     // this lane's partial row sum
+  f32x16 oacc[C::DBLK];
+#pragma unroll
+  for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+
+  if (ntiles > 0) {
+    load_regs(tile_at(0).kt);
+    store_regs(0);
+  }
+  __syncthreads();
+
+  // V^T transposed-read coordinates of this lane (see lds_read_tr16).
+  const int beta = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
+  const int tr_col = 16 * (beta & 1) + 4 * (s16 & 3);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const Tile cur = tile_at(t);
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) load_regs(tile_at(t + 1).kt);
+
+    if (trace_row != nullptr) {
+      if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
+      else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
+    }
+
+    // ---- S^T = K Q^T (64 keys x 32 queries per wave)
+    const bf16_t* kb_base = lds_k + buf * C::KT;
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb_base + (32 * kb + c) * C::KS + 16 * ds + 8 * g);
+        sacc[kb] = mfma32(ka, qf[ds], sacc[kb]);
+      }
+    }
+
+    // ---- scores in the exp2 domain.  Without modifiers the values stay raw
+    // dot products (the positive scale is applied inside the exponent).
+    constexpr bool kScaled = kAlibi || kSoftcap;
+    const int key0 = cur.kt * C::BN + 4 * g;  // key of register r is key0 + koff(kb, r)
+    if (kScaled) {
+      const float dist_base = static_cast<float>(my_q + delta - key0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float s = sacc[kb][r];
+          float x;
+          if (kSoftcap) {
+            // c * tanh(scale * s / c) in exp2 units; tanh(y) = 1 - 2 / (e^{2y} + 1)
+            const float e = fast_exp2(s * cap_k2);
+            x = cap_log2 * (1.0f - 2.0f * fast_rcp(e + 1.0f));
+          } else {
+            x = s * scale_log2;
+          }
+          if (kAlibi) {
+            const float koff = static_cast<float>(32 * kb + 8 * (r >> 2) + (r & 3));
+            x = __builtin_fmaf(-slope_log2, fabsf(dist_base - koff), x);
+          }
+          sacc[kb][r] = x;
+        }
+      }
+    }
+    if (!cur.full) {
+      const int* doc_t = lds_doc + buf * C::BN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const int j = key0 + koff;
+          const int i = my_q + delta;  // bottom-right aligned row position
+          bool ok = q_ok && j < a.Sk;
+          if (a.mask.causal) ok = ok && j <= i;
+          if (a.mask.wl >= 0) ok = ok && j >= i - a.mask.wl;
+          if (a.mask.wr >= 0) ok = ok && j <= i + a.mask.wr;
+          if (has_doc) ok = ok && doc_t[4 * g + koff] == doc_mine;
+          if (!ok) sacc[kb][r] = kNegInf;
+        }
+      }
+    }
+
+    // ---- online softmax
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float mx2 = kScaled ? mx : mx * scale_log2;  // -inf stays -inf
+    const bool need = mx2 > m_run + kRescaleThreshold;
+    if (__any(need)) {
+      const float m_new = fmaxf(m_run, mx2);
+      const float alpha = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float msub = (m_run == kNegInf) ? 0.0f : m_run;
+
+    bf16x8 pf[2][2];
+    float ls = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = kScaled ? fast_exp2(sacc[kb][r] - msub)
+                                : fast_exp2(__builtin_fmaf(sacc[kb][r], scale_log2, -msub));
+        ls += p;
+        pf[kb][r >> 3][r & 7] = static_cast<__bf16>(p);
+      }
+    }
+    l_run += ls;
+
+    // ---- O^T += V^T P^T
+    const bf16_t* vb_base = lds_v + buf * C::VT;
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16_t* p0 = vb_base + (32 * kb + 16 * ks + tr_row) * C::VS + 32 * db + tr_col;
+          const i16x4 lo = lds_read_tr16(p0);
+          const i16x4 hi = lds_read_tr16(p0 + 8 * C::VS);
+          const bf16x8 va = cat_frag(lo, hi);
+          oacc[db] = mfma32(va, pf[kb][ks], oacc[db]);
+        }
+      }
+    }
+
+    if (has_next) store_regs(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+  const float l_tot = l_run + wave_xor32(l_run);
+  if (q_ok) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)my_q * a.o_ss + h * a.o_sh;
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = 32 * db + 8 * rr + 4 * g;
+        uint2 packed;
+        packed.x = f32_to_bf16(oacc[db][4 * rr + 0] * inv) | (uint32_t)f32_to_bf16(oacc[db][4 * rr + 1] * inv) << 16;
+        packed.y = f32_to_bf16(oacc[db][4 * rr + 2] * inv) | (uint32_t)f32_to_bf16(oacc[db][4 * rr + 3] * inv) << 16;
+        *reinterpret_cast<uint2*>(op + d0) = packed;
+      }
+    }
+    if (g == 0)
+      a.lse[((int64_t)b * a.Hq + h) * a.Sq + my_q] =
+          l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
+  const int nqt = (a.Sq + kFwdBM - 1) / kFwdBM;
+  const dim3 grid(nqt * a.Hq * a.B), block(256);
+  const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0);
+  switch (mod) {
+    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<D, 0>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, 3>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+  if (a.Sq == 0 || a.B == 0 || a.Hq == 0) return hipSuccess;
+  if (a.D == 64) return launch_d<64>(a, s);
+  return launch_d<128>(a, s);
+}
+
+}  // namespace attn

@@ -1,0 +1,109 @@
+// Internal launch interfaces between the C-ABI layer (api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Mask predicate evaluated on partial tiles (causal / window / document).
+struct MaskArgs {
+  int causal, wl, wr;        // wl/wr < 0: unbounded side
+  const int32_t* doc_q;      // [B, Sq] or nullptr
+  const int32_t* doc_k;      // [B, Sk] or nullptr
+};
+
+// Block-sparse tile lists (nullptr kv_num_* = dense iteration).
+struct TileLists {
+  const int32_t* kv_num_full;
+  const int32_t* kv_idx_full;
+  const int32_t* kv_num_partial;
+  const int32_t* kv_idx_partial;
+  int nQ, nK;                // mask tile grid per batch row
+  int block_m;               // mask tile rows (a multiple of the kernel's)
+  int sub;                   // kernel key tiles per mask key tile
+};
+
+struct FwdArgs {
+  const void* q; const void* k; const void* v; void* o;
+  float* lse;
+  uint8_t* trace;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int B, Sq, Sk, Hq, Hkv, D;
+  int nQt, nKt;              // trace grid (kernel tiles, or mask tiles)
+  float scale;               // softmax scale (any sign)
+  const float* alibi;        // nullptr = off
+  int64_t alibi_sb;
+  float softcap;             // 0 = off
+  MaskArgs mask;
+  TileLists tiles;
+};
+
+// bf16 MFMA forward.  Tile 128 query rows x 64 keys.
+constexpr int kFwdBM = 128;
+constexpr int kFwdBN = 64;
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+
+// fp32 vector-ALU forward.  Tile 64 x 64.
+constexpr int kFwdF32BM = 64;
+constexpr int kFwdF32BN = 64;
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  const float* lse;
+  void* dq; void* dk; void* dv;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  int B, Sq, Sk, Hq, Hkv, D;
+  float scale;
+  const float* alibi;
+  int64_t alibi_sb;
+  float softcap;
+  MaskArgs mask;
+  float* delta;              // workspace [B, Hq, Sq]
+};
+size_t bwd_workspace_bytes(int B, int Hq, int Sq);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const void* q; const void* k; const void* v; void* o;
+  float* lse;
+  const int32_t* seqlens;
+  int64_t q_sb, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_sh;
+  int B, Hq, Hkv, D, Smax;
+  float scale;
+  float softcap;
+  int chunk;                 // keys per split
+  int max_splits;            // splits per sequence (grid extent)
+  float* part_o;             // workspace [B, max_splits, Hq, D]
+  float* part_lse;           // workspace [B, max_splits, Hq]
+};
+size_t decode_workspace_bytes(int B, int Hq, int D, int max_splits);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+struct BlockMaskArgs {
+  int B, Sq, Sk, bm, bn, nQ, nK;
+  MaskArgs mask;
+  uint8_t* cls;
+  int32_t* kv_num_partial; int32_t* kv_idx_partial;
+  int32_t* kv_num_full; int32_t* kv_idx_full;
+  int32_t* q_num_partial; int32_t* q_idx_partial;
+  int32_t* q_num_full; int32_t* q_idx_full;
+};
+hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,249 @@
+/*
+ * attn.h - C ABI of the exact IO-aware attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources cited below (web pages):
+ *   [TA]  "Accelerating AI: A Deep Dive into Flash Attention and Its Impacts"
+ *         (Towards AI)
+ *   [FA]  "FlashAttention: Fast and Memory-Efficient Exact Attention"
+ *         (Dao-AILab/flash-attention repository overview)
+ *   [HF]  "Improvements in attention_forward functions"
+ *         (huggingface/transformers issue 36218)
+ *   [GYM] "FlexAttention uses much more GPU memory than FlashAttention-2"
+ *         (pytorch-labs/attention-gym issue 101)
+ *   [FX4] "Lightning Talk: FlexAttention + FlashAttention-4: Fast and
+ *         Flexible" (PyTorch Conference Europe 2026)
+ *
+ * What is computed.  For batch b, query head h, query row i and key j, with
+ * g = h / (Hq / Hkv) the key/value head that h reads ([HF]: repeat_kv is a
+ * repeat_interleave over heads, here done by indexing, never by copying) and
+ * delta = Sk - Sq (last query aligned with the last key):
+ *
+ *   s   = scale * <q[b,i,h,:], k[b,j,g,:]>        scores, [TA] "Key-Value
+ *                                                 Attention"; scale per [FA]
+ *                                                 "Examples" (softmax_scale)
+ *   t   = softcap > 0 ? softcap * tanh(s / softcap) : s
+ *   u   = t - slope[b,h] * |i + delta - j|        if ALiBi slopes are given
+ *   allowed(i,j) = causal:  j <= i + delta
+ *                  window:  i + delta - left <= j <= i + delta + right
+ *                           (a side of -1 is unbounded; [FA] "Examples")
+ *                  block mask predicate (see attn_mask_desc) when given
+ *   lse[b,h,i] = log sum_{allowed j} exp(u)       natural log; -inf if none
+ *   o[b,i,h,:] = sum_{allowed j} exp(u - lse) * v[b,j,g,:]   (0 if none)
+ *
+ * computed tile by tile with an online softmax (running max and sum, [TA]
+ * "Tiling the Computation" and "2. Online Softmax") so the Sq x Sk score
+ * matrix never reaches device memory ([TA] "Enter Flash Attention").
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor and array arguments are DEVICE pointers unless stated.  The
+ *    caller allocates and owns every buffer (inputs, outputs, LSE,
+ *    workspace, block-mask arrays).  The library allocates nothing, frees
+ *    nothing, never synchronises the device, and enqueues all work on the
+ *    given stream (a hipStream_t passed as void*; NULL is the null stream).
+ *    Work is asynchronous: outputs are valid once the stream reaches them.
+ *  - Validation happens on the host before anything is enqueued.  On any
+ *    failure the function returns a non-zero status, stores a message
+ *    retrievable with attn_last_error() (thread-local), and enqueues
+ *    nothing, so outputs are untouched.
+ *  - attn_tensor strides are in ELEMENTS for the logical dims [B, S, H, D];
+ *    the D stride must be 1 and the base pointer and the B/S/H strides must
+ *    keep every row 16-byte aligned.  Any strides satisfying that are
+ *    accepted, so [B, H, S, D] views ([GYM] transposes q/k/v to that layout
+ *    for flex_attention) and packed-QKV slices ([FA] qkv of shape
+ *    (batch, seqlen, 3, nheads, headdim)) are read in place.
+ *  - Supported head dims: 64 and 128.  Supported dtypes: ATTN_BF16 for all
+ *    entry points; ATTN_FP32 for attn_fwd (computed in fp32 on the vector
+ *    ALU).  Every tensor of one call has the same dtype.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,   /* a shape, stride, pointer or flag is wrong */
+  ATTN_ERR_UNSUPPORTED = 2,   /* valid request this library does not cover */
+  ATTN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  ATTN_ERR_HIP = 4            /* the HIP runtime reported an error */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
+
+typedef struct {
+  void* data;          /* device pointer to element [0,0,0,0] */
+  int32_t dtype;       /* attn_dtype */
+  int64_t stride[4];   /* element strides of [B, S, H, D]; stride[3] == 1 */
+} attn_tensor;
+
+/* Mask predicate of a block-sparse mask ([GYM]: create_block_mask builds a
+ * mask from a mask_mod such as q_idx >= kv_idx; [FX4]: mask patterns such as
+ * causal and sliding window, evaluated inside the kernel).  The predicate is
+ * the AND of the enabled terms:
+ *   causal:   j <= i + (Sk - Sq)
+ *   window:   as in attn_params (-1 = unbounded side)
+ *   document: doc_q[b*Sq + i] == doc_k[b*Sk + j]  (device int32 arrays of
+ *             shape [B, Sq] and [B, Sk]; both NULL to disable)
+ * It does not depend on the head, so one mask serves every head. */
+typedef struct {
+  int32_t causal;
+  int32_t window_left, window_right;
+  const int32_t* doc_q;
+  const int32_t* doc_k;
+} attn_mask_desc;
+
+/* Block mask: every (block_m x block_n) tile of every batch row classified
+ * as 0 = EMPTY (no allowed pair; skipped), 1 = PARTIAL (predicate evaluated
+ * per element), 2 = FULL (inside [0,Sq) x [0,Sk) and every pair allowed; no
+ * predicate evaluated).  Lists are CSR-style per row of tiles, ascending,
+ * with the unused tail zero-filled:
+ *   cls            uint8 [B, nQ, nK]
+ *   kv_num_partial int32 [B, nQ]      kv_idx_partial int32 [B, nQ, nK]
+ *   kv_num_full    int32 [B, nQ]      kv_idx_full    int32 [B, nQ, nK]
+ *   q_num_partial  int32 [B, nK]      q_idx_partial  int32 [B, nK, nQ]
+ *   q_num_full     int32 [B, nK]      q_idx_full     int32 [B, nK, nQ]
+ * The struct itself is host memory; the arrays are device memory carved by
+ * block_mask_build() from one caller buffer. */
+typedef struct {
+  int32_t B, Sq, Sk, block_m, block_n, nQ, nK;
+  attn_mask_desc desc;
+  uint8_t* cls;
+  int32_t* kv_num_partial;
+  int32_t* kv_idx_partial;
+  int32_t* kv_num_full;
+  int32_t* kv_idx_full;
+  int32_t* q_num_partial;
+  int32_t* q_idx_partial;
+  int32_t* q_num_full;
+  int32_t* q_idx_full;
+} attn_block_mask;
+
+/* Problem description shared by attn_fwd / attn_bwd / attn_decode.
+ * Arguments follow flash_attn_func ([FA] "Examples"): q [B, Sq, Hq, D],
+ * k and v [B, Sk, Hkv, D] with Hq a multiple of Hkv (GQA/MQA). */
+typedef struct {
+  int32_t B, Sq, Sk, Hq, Hkv, D;
+  float softmax_scale;          /* NaN means 1/sqrt(D) (the page's None) */
+  int32_t causal;               /* bottom-right aligned when Sq != Sk */
+  int32_t window_left;          /* -1 = unbounded */
+  int32_t window_right;         /* -1 = unbounded */
+  const float* alibi_slopes;    /* device fp32, NULL = no ALiBi ([FA]:
+                                   (nheads,) or (batch, nheads)) */
+  int64_t alibi_batch_stride;   /* 0 for (Hq,), Hq for (B, Hq) */
+  float softcap;                /* 0 = off; else softcap * tanh(s/softcap) */
+  const attn_block_mask* block_mask;  /* NULL = dense; when given, causal
+                                   must be 0 and the window (-1,-1): the
+                                   mask's own predicate applies */
+} attn_params;
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(attn_status s);
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* ---------------------------------------------------------------------
+ * Forward ([TA] "Tiling the Computation", "2. Online Softmax",
+ * "3. Weighted Sum of Values"; [FA] flash_attn_func; [FX4] score and mask
+ * hooks, block-sparse iteration).
+ *   q, k, v : inputs as above.  o : output [B, Sq, Hq, D], same dtype.
+ *   lse     : output fp32 [B, Hq, Sq], contiguous, natural log.
+ *   tile_trace : NULL, or uint8 [B, Hq, nQt, nKt] (contiguous) that the
+ *             kernel fills with 1 / 2 for every tile it processed as
+ *             partial / full and leaves untouched for tiles it skipped (the
+ *             caller clears it).  nQt x nKt come from attn_fwd_tile_shape().
+ *   workspace : unused by the forward (may be NULL / 0).
+ * Errors: INVALID_ARG for inconsistent shapes, Hq % Hkv != 0, bad strides or
+ * alignment, window < -1, softcap < 0 or non-finite, a block mask whose
+ * B/Sq/Sk differ or combined with causal/window; UNSUPPORTED for D not in
+ * {64, 128}, or a block mask tile other than block_m = 128 and block_n a
+ * multiple of 64 (bf16) / 64 x 64 (fp32). */
+attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k,
+                     attn_tensor v, attn_tensor o, float* lse,
+                     uint8_t* tile_trace, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Query / key tile sizes the forward uses for this problem (host only).
+ * The tile trace has ceil(Sq/block_m) x ceil(Sk/block_n) entries per head. */
+attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype,
+                                int32_t* block_m, int32_t* block_n);
+
+/* ---------------------------------------------------------------------
+ * Backward from the saved LSE ([FX4]: the backward reuses the forward's
+ * machinery; [FA]: deterministic backward flag).  Gradients of
+ * sum(o * dout) with respect to q, k, v:
+ *   dv[j,g] = sum_{h in g} sum_i P_ij dout_i
+ *   dP_ij = <dout_i, v_j>;  Delta_i = <dout_i, o_i>
+ *   dS_ij = P_ij (dP_ij - Delta_i) * (softcap ? 1 - tanh^2(s_ij/softcap) : 1)
+ *   dq_i = scale sum_j dS_ij k_j;  dk[j,g] = scale sum_{h in g} sum_i dS_ij q_i
+ * with P_ij = exp(u_ij - lse_i) recomputed tile by tile.  dk/dv of a kv head
+ * sum the G query heads that read it.
+ *   o, lse : the forward's outputs for the same inputs.
+ *   dq, dk, dv : outputs, same shapes and dtype as q, k, v.
+ *   deterministic : must be 1 (the only implemented schedule: every output
+ *             element is reduced in a fixed order without atomics, so
+ *             repeated calls are bitwise identical).
+ *   workspace : at least attn_bwd_workspace_size(p) bytes, 256-byte aligned.
+ * Errors: as attn_fwd; UNSUPPORTED for fp32 inputs, block masks or
+ * deterministic == 0; WORKSPACE if too small. */
+attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k,
+                     attn_tensor v, attn_tensor o, attn_tensor dout,
+                     const float* lse, attn_tensor dq, attn_tensor dk,
+                     attn_tensor dv, int32_t deterministic, void* workspace,
+                     size_t workspace_bytes, void* stream);
+size_t attn_bwd_workspace_size(const attn_params* p);
+
+/* ---------------------------------------------------------------------
+ * Decode over a KV cache ([FA] flash_attn_with_kvcache: q attends to the
+ * first cache_seqlens[b] rows of its batch row of k_cache / v_cache; no
+ * backward).  Split-K: each sequence's cache prefix is cut into chunks that
+ * are attended independently, and the chunk results are merged with the
+ * LSE-weighted combine  lse = log sum_s exp(lse_s),
+ * o = sum_s exp(lse_s - lse) o_s.
+ *   p : B, Sq (== 1), Hq, Hkv, D as usual; Sk = cache capacity Smax;
+ *       scale and softcap apply; causal, window, ALiBi and block masks are
+ *       not supported by this entry point (UNSUPPORTED).
+ *   q : [B, 1, Hq, D];  k_cache, v_cache : [B, Smax, Hkv, D].
+ *   cache_seqlens : device int32 [B], each in [0, Smax] (values outside are
+ *       clamped to that range on the device).  A sequence of length 0 gives
+ *       o = 0 and lse = -inf.
+ *   num_splits : keys per split is chosen by the library when 0; otherwise
+ *       the maximum number of splits per sequence (>= 1).
+ *   o : [B, 1, Hq, D];  lse : fp32 [B, Hq, 1] contiguous.
+ *   workspace : at least attn_decode_workspace_size(p, num_splits) bytes.
+ */
+attn_status attn_decode(const attn_params* p, attn_tensor q,
+                        attn_tensor k_cache, attn_tensor v_cache,
+                        const int32_t* cache_seqlens, int32_t num_splits,
+                        attn_tensor o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits);
+
+/* ---------------------------------------------------------------------
+ * Block-mask construction on the device ([GYM] create_block_mask with
+ * BLOCK_SIZE; [FX4] block-sparse masks skip tiles with nothing to compute).
+ * Classifies every tile by evaluating the predicate of `m` on every in-bounds
+ * pair of the tile (a tile crossing the end of the sequence is never FULL),
+ * then writes the ascending CSR lists (forward and transposed).
+ *   buffer : device memory of at least attn_block_mask_bytes(...) bytes,
+ *            256-byte aligned; `out` (host struct) receives the header and
+ *            pointers into it.
+ * Errors: INVALID_ARG for non-positive sizes, window < -1, only one of
+ * doc_q / doc_k given; WORKSPACE if the buffer is too small. */
+size_t attn_block_mask_bytes(int32_t B, int32_t Sq, int32_t Sk,
+                             int32_t block_m, int32_t block_n);
+attn_status block_mask_build(const attn_mask_desc* m, int32_t B, int32_t Sq,
+                             int32_t Sk, int32_t block_m, int32_t block_n,
+                             void* buffer, size_t buffer_bytes,
+                             attn_block_mask* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

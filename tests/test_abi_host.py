@@ -1,0 +1,214 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function
+include/attn.h declares, and rejects bad arguments before touching the
+device (validation paths are exercised with fake, never-dereferenced
+pointers, so no GPU is needed)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "exact_attention_10_amd", "libattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libattn.so not built")
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:attn_status|size_t|const char\*)\s+(\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_all_declared_symbols_exported():
+    from exact_attention_10_amd import binding
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED)
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.fixture(scope="module")
+def b():
+    from exact_attention_10_amd import binding
+    return binding
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def tensor(b, shape, dtype=0, strides=None, ptr=FAKE):
+    t = b.attn_tensor()
+    t.data = ptr
+    t.dtype = dtype
+    if strides is None:
+        strides = [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+    for i in range(4):
+        t.stride[i] = strides[i]
+    return t
+
+
+def params(b, B=1, Sq=128, Sk=128, Hq=4, Hkv=2, D=64, **kw):
+    p = b.attn_params()
+    p.B, p.Sq, p.Sk, p.Hq, p.Hkv, p.D = B, Sq, Sk, Hq, Hkv, D
+    p.softmax_scale = math.nan
+    p.causal = kw.get("causal", 0)
+    p.window_left, p.window_right = kw.get("window", (-1, -1))
+    p.alibi_slopes = kw.get("alibi", None)
+    p.alibi_batch_stride = kw.get("alibi_sb", 0)
+    p.softcap = kw.get("softcap", 0.0)
+    p.block_mask = None
+    return p
+
+
+def fwd(b, p, q=None, k=None, v=None, o=None, lse=FAKE):
+    q = q or tensor(b, (p.B, p.Sq, p.Hq, p.D))
+    k = k or tensor(b, (p.B, p.Sk, p.Hkv, p.D))
+    v = v or tensor(b, (p.B, p.Sk, p.Hkv, p.D))
+    o = o or tensor(b, (p.B, p.Sq, p.Hq, p.D))
+    lib = b.library()
+    st = lib.attn_fwd(ctypes.byref(p), q, k, v, o, lse, None, None, 0, None)
+    return st, lib.attn_last_error().decode()
+
+
+def test_status_strings(b):
+    lib = b.library()
+    assert lib.attn_status_string(0) == b"ATTN_OK"
+    assert lib.attn_status_string(3) == b"ATTN_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda p: setattr(p, "Hkv", 3), 1, "multiple"),
+    (lambda p: setattr(p, "D", 96), 2, "head dim"),
+    (lambda p: setattr(p, "window_left", -2), 1, "window"),
+    (lambda p: setattr(p, "softcap", -1.0), 1, "softcap"),
+    (lambda p: setattr(p, "softcap", float("inf")), 1, "softcap"),
+    (lambda p: setattr(p, "softmax_scale", float("inf")), 1, "scale"),
+    (lambda p: setattr(p, "Sq", -1), 1, "negative"),
+    (lambda p: setattr(p, "Hq", 0), 1, "positive"),
+])
+def test_fwd_rejects_bad_params(b, mutate, status, msg):
+    p = params(b)
+    mutate(p)
+    st, err = fwd(b, p)
+    assert st == status and msg in err, (st, err)
+
+
+def test_fwd_rejects_bad_tensors(b):
+    p = params(b)
+    st, err = fwd(b, p, q=tensor(b, (1, 128, 4, 64), strides=[128 * 256, 256, 64, 2]))
+    assert st == 1 and "head-dim stride" in err
+    st, err = fwd(b, p, q=tensor(b, (1, 128, 4, 64), ptr=FAKE + 8))
+    assert st == 1 and "aligned" in err
+    st, err = fwd(b, p, q=tensor(b, (1, 128, 4, 64), strides=[128 * 260, 260, 65, 1]))
+    assert st == 1 and "16 bytes" in err
+    st, err = fwd(b, p, k=tensor(b, (1, 128, 2, 64), dtype=1))
+    assert st == 1 and "dtype" in err
+    st, err = fwd(b, p, v=tensor(b, (1, 128, 2, 64), ptr=0))
+    assert st == 1 and "null" in err
+    st, err = fwd(b, p, lse=None)
+    assert st == 1 and "lse" in err
+    st, err = fwd(b, params(b, alibi=FAKE, alibi_sb=3))
+    assert st == 1 and "alibi" in err
+
+
+def test_bwd_validation(b):
+    lib = b.library()
+    p = params(b)
+    t = lambda S, H: tensor(b, (1, S, H, 64))
+    args = [t(128, 4), t(128, 2), t(128, 2), t(128, 4), t(128, 4), FAKE, t(128, 4), t(128, 2),
+            t(128, 2)]
+    need = lib.attn_bwd_workspace_size(ctypes.byref(p))
+    assert need >= 1 * 4 * 128 * 4
+    st = lib.attn_bwd(ctypes.byref(p), *args, 1, None, 0, None)
+    assert st == 3 and b"workspace" in lib.attn_last_error()
+    st = lib.attn_bwd(ctypes.byref(p), *args, 0, FAKE, need, None)
+    assert st == 2 and b"deterministic" in lib.attn_last_error()
+    st = lib.attn_bwd(ctypes.byref(p), *args, 1, FAKE + 16, need, None)
+    assert st == 3 and b"aligned" in lib.attn_last_error()
+    fp32 = [tensor(b, (1, 128, h, 64), dtype=1) for h in (4, 2, 2, 4, 4)]
+    st = lib.attn_bwd(ctypes.byref(p), *fp32, FAKE, *[tensor(b, (1, 128, h, 64), dtype=1) for h in (4, 2, 2)],
+                      1, FAKE, need, None)
+    assert st == 2
+
+
+def test_decode_validation(b):
+    lib = b.library()
+    p = params(b, B=4, Sq=1, Sk=1024, Hq=8, Hkv=1, D=128)
+    q = tensor(b, (4, 1, 8, 128))
+    kc = tensor(b, (4, 1024, 1, 128))
+    need = lib.attn_decode_workspace_size(ctypes.byref(p), 0)
+    assert need > 0
+    st = lib.attn_decode(ctypes.byref(p), q, kc, kc, FAKE, 0, q, FAKE, None, 0, None)
+    assert st == 3
+    p2 = params(b, B=4, Sq=2, Sk=1024, Hq=8, Hkv=1, D=128)
+    st = lib.attn_decode(ctypes.byref(p2), tensor(b, (4, 2, 8, 128)), kc, kc, FAKE, 0,
+                         tensor(b, (4, 2, 8, 128)), FAKE, FAKE, need, None)
+    assert st == 2
+    p3 = params(b, B=4, Sq=1, Sk=1024, Hq=8, Hkv=1, D=128, causal=1)
+    st = lib.attn_decode(ctypes.byref(p3), q, kc, kc, FAKE, 0, q, FAKE, FAKE, need, None)
+    assert st == 2
+    st = lib.attn_decode(ctypes.byref(p), q, kc, kc, None, 0, q, FAKE, FAKE, need, None)
+    assert st == 1
+    # more splits need at least as much workspace
+    assert lib.attn_decode_workspace_size(ctypes.byref(p), 16) >= \
+        lib.attn_decode_workspace_size(ctypes.byref(p), 1)
+
+
+def test_block_mask_validation_and_sizes(b):
+    lib = b.library()
+    d = b.attn_mask_desc()
+    d.causal, d.window_left, d.window_right = 1, -1, -1
+    d.doc_q, d.doc_k = None, None
+    out = b.attn_block_mask()
+    n = lib.attn_block_mask_bytes(2, 8192, 8192, 128, 128)
+    nq = nk = 64
+    up = lambda x: (x + 255) // 256 * 256
+    assert n == up(2 * nq * nk) + 2 * (up(2 * nq * 4) + up(2 * nq * nk * 4)) + \
+        2 * (up(2 * nk * 4) + up(2 * nk * nq * 4))
+    assert lib.block_mask_build(ctypes.byref(d), 2, 8192, 8192, 128, 128, FAKE, n - 1,
+                                ctypes.byref(out), None) == 3
+    assert lib.block_mask_build(ctypes.byref(d), 0, 8192, 8192, 128, 128, FAKE, n,
+                                ctypes.byref(out), None) == 1
+    d.doc_q = FAKE
+    assert lib.block_mask_build(ctypes.byref(d), 2, 8192, 8192, 128, 128, FAKE, n,
+                                ctypes.byref(out), None) == 1
+    d.doc_q = None
+    d.window_left = -3
+    assert lib.block_mask_build(ctypes.byref(d), 2, 8192, 8192, 128, 128, FAKE, n,
+                                ctypes.byref(out), None) == 1
+
+
+def test_block_mask_forward_validation(b):
+    lib = b.library()
+    bm = b.attn_block_mask()
+    bm.B, bm.Sq, bm.Sk, bm.block_m, bm.block_n, bm.nQ, bm.nK = 1, 128, 128, 128, 128, 1, 1
+    for f in ("kv_num_full", "kv_idx_full", "kv_num_partial", "kv_idx_partial"):
+        setattr(bm, f, FAKE)
+    p = params(b)
+    p.block_mask = ctypes.pointer(bm)
+    p.causal = 1
+    st, err = fwd(b, p)
+    assert st == 1 and "own predicate" in err
+    p.causal = 0
+    bm.block_n = 96
+    bm.nK = 2
+    st, err = fwd(b, p)
+    assert st == 2
+    bm.block_n, bm.nK, bm.Sk = 128, 1, 256
+    st, err = fwd(b, p)
+    assert st == 1 and "built for" in err
+
+
+def test_tile_shape(b):
+    lib = b.library()
+    p = params(b)
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.attn_fwd_tile_shape(ctypes.byref(p), 0, ctypes.byref(bm), ctypes.byref(bn)) == 0
+    assert (bm.value, bn.value) == (128, 64)
+    assert lib.attn_fwd_tile_shape(ctypes.byref(p), 1, ctypes.byref(bm), ctypes.byref(bn)) == 0
+    assert (bm.value, bn.value) == (64, 64)

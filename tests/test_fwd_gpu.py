@@ -1,0 +1,238 @@
+"""GPU parity of the forward kernels and the device block mask against the
+fp64 oracle (through the C ABI via the ctypes binding)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_10_amd import inputs
+from helpers import check_lse, check_o, f64, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_10_amd import binding
+    return binding
+
+
+def run_fwd(b, w, trace=False, **kw):
+    q = to_device(w["q"], w["dtype"], torch)
+    k = to_device(w["k"], w["dtype"], torch)
+    v = to_device(w["v"], w["dtype"], torch)
+    tr = None
+    if trace:
+        bm, bn = b.tile_shape(q, k, kw.get("block_mask"))
+        nq = -(-q.shape[1] // bm)
+        nk = -(-k.shape[1] // bn)
+        tr = torch.zeros((q.shape[0], q.shape[2], nq, nk), dtype=torch.uint8, device="cuda")
+    o, lse = b.attn_fwd(q, k, v, tile_trace=tr, **kw)
+    torch.cuda.synchronize()
+    return o, lse, tr
+
+
+def expected_trace(B, Hq, Sq, Sk, bm, bn, causal=False, window=(-1, -1), doc=None):
+    cls = oracle.block_mask(B, Sq, Sk, bm, bn, causal=causal, window=window,
+                            doc_q=doc, doc_k=doc)["cls"]
+    return np.broadcast_to(cls[:, None], (B, Hq) + cls.shape[1:])
+
+
+def test_tiny_dense_fp32(b):
+    """128 x 128, two heads, fp32, non-causal: vector-ALU fp32 path."""
+    w = inputs.tiny_dense()
+    o, lse, _ = run_fwd(b, w, softmax_scale=w["scale"])
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=w["scale"])
+    assert check_o(to_f64(o), O) < 1e-5
+    assert check_lse(to_f64(lse), L) < 1e-5
+
+
+CASES = [
+    # B, Sq, Sk, Hq, Hkv, D, options
+    (1, 128, 128, 2, 2, 64, {}),
+    (2, 200, 333, 4, 2, 64, {}),
+    (1, 257, 257, 8, 2, 128, {"causal": True}),
+    (2, 300, 190, 4, 1, 128, {"causal": True}),          # Sq > Sk: empty rows
+    (1, 190, 300, 4, 4, 64, {"causal": True}),           # Sq < Sk: bottom-right
+    (1, 400, 400, 4, 2, 128, {"causal": True, "window": (100, 0)}),
+    (1, 333, 333, 2, 1, 64, {"window": (70, 33)}),
+    (1, 256, 256, 2, 2, 128, {"window": (0, 0)}),
+    (1, 300, 300, 4, 2, 128, {"causal": True, "alibi": True}),
+    (1, 300, 260, 4, 2, 64, {"alibi": True, "window": (50, 20)}),
+    (1, 300, 300, 4, 2, 128, {"causal": True, "softcap": 5.0}),
+    (1, 280, 280, 4, 4, 64, {"causal": True, "softcap": 2.0, "alibi": True}),
+    (1, 65, 1, 2, 1, 128, {}),                           # a single key
+    (1, 1, 700, 8, 1, 128, {}),                          # a single query
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_fwd_bf16_parity_and_trace(b, case):
+    B, Sq, Sk, Hq, Hkv, D, opt = case
+    w = inputs.random_case(100 + Sq + Sk + D, B, Sq, Sk, Hq, Hkv, D, dtype="bf16")
+    scale = 0.11 if D == 128 else 0.15
+    kw = dict(softmax_scale=scale, causal=opt.get("causal", False),
+              window=opt.get("window", (-1, -1)), softcap=opt.get("softcap", 0.0))
+    slopes = None
+    if opt.get("alibi"):
+        slopes = np.exp2(-8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+    o, lse, tr = run_fwd(b, w, trace=True, **kw)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=scale,
+                                causal=kw["causal"], window=kw["window"],
+                                alibi_slopes=slopes, softcap=kw["softcap"])
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    exp = expected_trace(B, Hq, Sq, Sk, 128, 64, kw["causal"], kw["window"])
+    np.testing.assert_array_equal(tr.cpu().numpy(), exp)
+
+
+def test_fwd_negative_scale_and_strided_views(b):
+    """Negative softmax scale; q/k/v given as [B, H, S, D]-contiguous views
+    (the Flex layout) and as slices of a packed [B, S, 3, H, D] tensor."""
+    B, S, H, D = 1, 200, 4, 64
+    w = inputs.random_case(7, B, S, S, H, H, D, dtype="bf16")
+    q = to_device(w["q"], "bf16", torch)
+    k = to_device(w["k"], "bf16", torch)
+    v = to_device(w["v"], "bf16", torch)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=-0.2, causal=True)
+    qt = q.transpose(1, 2).contiguous().transpose(1, 2)
+    kt = k.transpose(1, 2).contiguous().transpose(1, 2)
+    vt = v.transpose(1, 2).contiguous().transpose(1, 2)
+    o, lse = b.attn_fwd(qt, kt, vt, softmax_scale=-0.2, causal=True)
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    packed = torch.stack([q, k, v], dim=2)  # [B, S, 3, H, D]
+    o2, lse2 = b.attn_fwd(packed[:, :, 0], packed[:, :, 1], packed[:, :, 2],
+                          softmax_scale=-0.2, causal=True)
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)
+
+
+def test_fwd_empty_inputs(b):
+    q = torch.zeros((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 10, 2, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = b.attn_fwd(q, k, k)
+    assert o.numel() == 0
+    q = torch.randn((1, 5, 2, 64), device="cuda").to(torch.bfloat16)
+    k0 = torch.zeros((1, 0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = b.attn_fwd(q, k0, k0)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_fwd_llama8b_causal_full(b):
+    """B=1, Hq=32, Hkv=8, S=2048, D=128, causal: every output against the oracle,
+    the skipped/partial/full tile sets bit-exact, and two runs bitwise equal."""
+    w = inputs.llama8b_train()
+    o, lse, tr = run_fwd(b, w, trace=True, softmax_scale=w["scale"], causal=True)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=w["scale"],
+                                causal=True)
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    np.testing.assert_array_equal(tr.cpu().numpy(),
+                                  expected_trace(1, 32, 2048, 2048, 128, 64, True))
+    o2, lse2, _ = run_fwd(b, w, softmax_scale=w["scale"], causal=True)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.fixture(scope="module")
+def long_local():
+    return inputs.long_local()
+
+
+@pytest.mark.parametrize("mod", ["alibi", "softcap"])
+def test_fwd_long_local_sampled(b, long_local, mod):
+    """S=16384, causal + window (4096, 0), ALiBi or softcap 50: sampled rows of
+    8 heads (first/last rows, tile edges, window edge) against the oracle;
+    the tile trace of all heads against the closed-form tile classes."""
+    w = long_local
+    kw = dict(softmax_scale=w["scale"], causal=True, window=(4096, 0))
+    slopes = None
+    if mod == "alibi":
+        slopes = w["alibi_slopes"]
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+    else:
+        kw["softcap"] = w["softcap"]
+    o, lse, tr = run_fwd(b, w, trace=True, **kw)
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    q, k, v = f64(w, "q"), f64(w, "k"), f64(w, "v")
+    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 4096, 4097, 8191, 8192, 12345, 16320, 16383])
+    for h in (0, 5, 10, 15, 16, 21, 27, 31):
+        Or, Lr = oracle.attention_fwd_rows(q, k, v, 0, h, rows, scale=w["scale"], causal=True,
+                                           window=(4096, 0), alibi_slopes=slopes,
+                                           softcap=kw.get("softcap", 0.0))
+        check_o(o[0, rows, h], Or, what="O[h=%d]" % h)
+        check_lse(lse[0, h, rows], Lr)
+    exp = expected_trace(1, 32, 16384, 16384, 128, 64, True, (4096, 0))
+    np.testing.assert_array_equal(tr.cpu().numpy(), exp)
+
+
+@pytest.fixture(scope="module")
+def doc_mask():
+    return inputs.doc_mask()
+
+
+def test_block_mask_device_bit_exact(b, doc_mask):
+    """Document + causal 128 x 128 block mask built on the device equals the
+    oracle's brute-force classification and CSR lists, every array bit-exact."""
+    w = doc_mask
+    doc = torch.from_numpy(w["doc"]).cuda()
+    m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
+    got = {k2: v2.cpu().numpy() for k2, v2 in m.arrays().items()}
+    exp = oracle.block_mask(2, 8192, 8192, 128, 128, causal=True, doc_q=w["doc"], doc_k=w["doc"])
+    for name, arr in exp.items():
+        np.testing.assert_array_equal(got[name], arr, err_msg=name)
+
+
+@pytest.mark.parametrize("shape", [(1, 300, 300, 64, 64, True, (-1, -1)),
+                                   (2, 250, 390, 32, 96, False, (40, 7)),
+                                   (1, 129, 77, 128, 128, True, (5, -1))])
+def test_block_mask_device_small(b, shape):
+    B, Sq, Sk, bm, bn, causal, window = shape
+    m = b.block_mask_build(B, Sq, Sk, bm, bn, causal=causal, window=window)
+    got = {k2: v2.cpu().numpy() for k2, v2 in m.arrays().items()}
+    exp = oracle.block_mask(B, Sq, Sk, bm, bn, causal=causal, window=window)
+    for name, arr in exp.items():
+        np.testing.assert_array_equal(got[name], arr, err_msg=name)
+
+
+def test_fwd_doc_block_sparse(b, doc_mask):
+    """Block-sparse document mask forward: sampled rows of every head against
+    the oracle; visited tiles (trace) equal to the non-empty mask tiles."""
+    w = doc_mask
+    doc = torch.from_numpy(w["doc"]).cuda()
+    m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
+    o, lse, tr = run_fwd(b, w, trace=True, softmax_scale=w["scale"], block_mask=m)
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    q, k, v = f64(w, "q"), f64(w, "k"), f64(w, "v")
+    for bb in range(2):
+        rows = np.unique(np.concatenate([[0, 1, 127, 128, 4000, 8191],
+                                         np.cumsum(w["doc_lengths"][bb])[:-1],
+                                         np.cumsum(w["doc_lengths"][bb])[:-1] - 1]))
+        for h in range(0, 16, 3):
+            Or, Lr = oracle.attention_fwd_rows(q, k, v, bb, h, rows, scale=w["scale"],
+                                               causal=True, doc_q=w["doc"], doc_k=w["doc"])
+            check_o(o[bb, rows, h], Or)
+            check_lse(lse[bb, h, rows], Lr)
+    exp = expected_trace(2, 16, 8192, 8192, 128, 128, True, doc=w["doc"])
+    np.testing.assert_array_equal(tr.cpu().numpy(), exp)
+
+
+def test_fwd_doc_block_sparse_small_full(b):
+    """Small ragged document mask (partial last tiles): every output."""
+    w = inputs.random_case(21, 2, 300, 300, 4, 2, 64, dtype="bf16", doc_len_range=(20, 90))
+    doc = torch.from_numpy(w["doc"]).cuda()
+    m = b.block_mask_build(2, 300, 300, 128, 128, causal=True, doc_q=doc, doc_k=doc)
+    o, lse, tr = run_fwd(b, w, trace=True, softmax_scale=0.125, block_mask=m)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=0.125, causal=True,
+                                doc_q=w["doc"], doc_k=w["doc"])
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    np.testing.assert_array_equal(tr.cpu().numpy(),
+                                  expected_trace(2, 4, 300, 300, 128, 128, True, doc=w["doc"]))
