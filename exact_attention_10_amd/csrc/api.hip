@@ -271,13 +271,19 @@ attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
   a.alibi_sb = p->alibi_batch_stride;
   a.softcap = p->softcap;
   a.mask = mask_from(p);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   a.delta = static_cast<float*>(workspace);
+  char* rest = static_cast<char*>(workspace) + up((size_t)p->B * p->Hq * p->Sq * sizeof(float));
+  const size_t part = up((size_t)p->B * p->Sk * p->Hq * p->D * sizeof(float));
+  a.part_dk = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest) : nullptr;
+  a.part_dv = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest + part) : nullptr;
   return hip_status(attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
 }
 
 size_t attn_bwd_workspace_size(const attn_params* p) {
-  if (p == nullptr || p->B < 0 || p->Hq < 0 || p->Sq < 0) return 0;
-  return attn::bwd_workspace_bytes(p->B, p->Hq, p->Sq);
+  if (p == nullptr || p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Sq < 0 || p->Sk < 0 || p->D <= 0)
+    return 0;
+  return attn::bwd_workspace_bytes(p->B, p->Hq, p->Hkv, p->Sq, p->Sk, p->D);
 }
 
 // Keys per split for decode when the caller does not choose: enough splits

@@ -72,8 +72,10 @@ struct BwdArgs {
   float softcap;
   MaskArgs mask;
   float* delta;              // workspace [B, Hq, Sq]
+  float* part_dk;            // workspace [B, Sk, Hq, D] (grouped heads only)
+  float* part_dv;
 };
-size_t bwd_workspace_bytes(int B, int Hq, int Sq);
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 
 struct DecodeArgs {
