@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X (gfx950).
+
+A step is one forward and one backward pass over the Llama-3.1-8B-shaped
+training attention (B=1, Hq=32, Hkv=8, S=2048, D=128, bf16, causal): attn_fwd,
+then the four stages of attn_bwd.  Inputs are seeded synthetic N(0, 1) bf16
+tensors resident in device memory before timing starts.  W untimed steps, then
+K timed steps between two device synchronisations.  Throughput counts
+4*D flops per allowed (query, key) pair and head for the forward and 2.5x that
+for the backward (QK^T, PV; and QK^T, dO V^T, P^T dO, dS^T Q, dS K).
+
+Besides the headline line the JSON carries:
+  roofline      the dominant kernel's achieved rate against the bf16 MFMA
+                peak, timed with HIP events around that kernel's own launches
+                inside the timed steps;
+  kernels       per-kernel times and rates from the same events;
+  extra         the other workloads: split-K decode over a KV cache (HBM
+                GB/s, 8 rotating cache copies so the 256 MB last-level cache
+                cannot hold the working set), long-context local attention
+                with ALiBi / softcap, the packed-document block-sparse mask
+                (device mask build and forward);
+  cpu_baseline  the fp64 CPU oracle timed on this host on one full step of the
+                same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+                       [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+METRIC = ("attention fwd/bwd TFLOP/s and % bf16 MFMA peak; decode HBM GB/s (1 MI355X)")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Prepared:
+    """ctypes argument tuples built once, so the timed loop only enqueues."""
+
+    def __init__(self, fn, args):
+        self.fn = fn
+        self.args = args
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            from exact_attention_10_amd import binding
+            raise binding.AttnError(st, binding.library().attn_last_error().decode())
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_10_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, src_hash, per_launch_units):
+    """HBM bytes per launch from committed counter summaries, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; runs on %d GPUs are not part of this benchmark "
+              "(the kernels shard by batch and kv head with no communication)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from exact_attention_10_amd import binding as b
+    from exact_attention_10_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = b.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- headline workload: fwd + bwd, B1 Hq32 Hkv8 S2048 D128 causal
+    w = inputs.llama8b_train()
+    q, k, v, do = (to_dev(w[n]) for n in ("q", "k", "v", "do"))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    p = b._params(q, k, D, w["scale"], True, (-1, -1), None, 0.0, None)
+    ws_bytes = lib.attn_bwd_workspace_size(ctypes.byref(p))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    T = b._tensor
+    fwd = Prepared(lib.attn_fwd, (ctypes.byref(p), T(q), T(k), T(v), T(o), b._ptr(lse), None,
+                                  None, 0, stream))
+    bwd_args = (ctypes.byref(p), T(q), T(k), T(v), T(o), T(do), b._ptr(lse), T(dq), T(dk), T(dv),
+                1, b._ptr(ws), ws_bytes)
+    stages = [Prepared(lib.attn_bwd_stage, bwd_args + (st, stream)) for st in range(4)]
+
+    pairs = S * (S + 1) // 2
+    fwd_flops = 4.0 * B * Hq * D * pairs
+    bwd_flops = 2.5 * fwd_flops
+    names = ["fwd", "bwd_delta", "bwd_dkdv", "bwd_group_sum", "bwd_dq"]
+    # Contractions each kernel executes per allowed pair and head (recomputed
+    # products included): forward QK^T, PV; dK/dV: QK^T, dO V^T, P^T dO,
+    # dS^T Q; dQ: QK^T, dO V^T, dS K.
+    kernel_flops = {"fwd": fwd_flops, "bwd_dkdv": 2.0 * fwd_flops, "bwd_dq": 1.5 * fwd_flops}
+    src = {"fwd": ("fwd_bf16.hip", "common.h"), "bwd_dkdv": ("bwd_bf16.hip", "common.h"),
+           "bwd_dq": ("bwd_bf16.hip", "common.h")}
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fwd()
+        for i, st in enumerate(stages):
+            if ev is not None:
+                ev[i + 1].record()
+            st()
+        if ev is not None:
+            ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    per_kernel_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                     for i, n in enumerate(names)}
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for n, ms in per_kernel_ms.items():
+        rec = {"ms": round(ms, 5)}
+        if n in kernel_flops:
+            rec["tflops"] = round(kernel_flops[n] / (ms * 1e-3) / 1e12, 2)
+        kernels[n] = rec
+    kernels["fwd"]["tflops_counted"] = kernels["fwd"]["tflops"]
+    bwd_ms = sum(per_kernel_ms[n] for n in names[1:])
+    kernels["bwd_total"] = {"ms": round(bwd_ms, 5),
+                            "tflops_counted": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)}
+
+    dom = max(kernel_flops, key=lambda n: per_kernel_ms[n])
+    achieved = kernel_flops[dom] / (per_kernel_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom, source_hash(*src[dom]), 1)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3.1-8b attention fwd+bwd: B=1 Hq=32 Hkv=8 S=2048 D=128 "
+                               "causal bf16", "global_batch": B, "seq_len": S,
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+
+    del ws, dq, dk, dv
+    if not args.no_extra:
+        out["extra"] = extra_workloads(b, lib, inputs, torch, np, dev, to_dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, fwd_flops + bwd_flops)
+    print(json.dumps(out), flush=True)
+
+
+def timed(torch, np, fn, reps, warm=2):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    ts = [s.elapsed_time(e) for s, e in evs]
+    return float(np.median(ts)), float(np.min(ts))
+
+
+def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
+    ex = {}
+    # decode: B=32, Hq=128, Hkv=1, D=128, cache lengths in [1024, 8192]
+    w = inputs.decode_mqa()
+    lens = torch.from_numpy(w["cache_seqlens"]).to(dev)
+    total = int(w["cache_seqlens"].sum())
+    Bd, _, Hqd, Dd = w["q"].shape
+    copies = []
+    for _ in range(8):
+        copies.append((to_dev(w["q"]), to_dev(w["k"]), to_dev(w["v"])))
+    o = torch.empty_like(copies[0][0])
+    lse = torch.empty((Bd, Hqd, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(b.decode_workspace_size(copies[0][0], copies[0][1]), dtype=torch.uint8,
+                     device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = []
+    for qq, kk, vv in copies:
+        p = b._params(qq, kk, Dd, w["scale"], False, (-1, -1), None, 0.0, None)
+        calls.append(Prepared(lib.attn_decode, (ctypes.byref(p), b._tensor(qq), b._tensor(kk),
+                                                b._tensor(vv), b._ptr(lens), 0, b._tensor(o),
+                                                b._ptr(lse), b._ptr(ws), ws.numel(), stream)))
+        calls[-1].keep = p
+    it = [0]
+
+    def dec():
+        calls[it[0] % 8]()
+        it[0] += 1
+
+    med, mn = timed(torch, np, dec, 40)
+    algo_bytes = total * Dd * 2 * 2 + 2 * Bd * Hqd * Dd * 2 + Bd * Hqd * 4
+    ex["decode_mqa_b32_h128"] = {
+        "ms": round(med, 5), "ms_min": round(mn, 5),
+        "hbm_gbs": round(algo_bytes / (med * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(algo_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "tflops": round(4.0 * Hqd * Dd * total / (med * 1e-3) / 1e12, 2),
+        "algorithmic_bytes": algo_bytes}
+    del copies, o, ws
+
+    # long-context local attention: S=16384, causal + window (4096, 0)
+    w = inputs.long_local()
+    q, k, v = to_dev(w["q"]), to_dev(w["k"]), to_dev(w["v"])
+    oo = torch.empty_like(q)
+    ll = torch.empty((1, 32, 16384), dtype=torch.float32, device=dev)
+    slopes = torch.from_numpy(w["alibi_slopes"]).to(dev)
+    pairs = 4096 * 4097 // 2 + (16384 - 4096) * 4097
+    fl = 4.0 * 32 * 128 * pairs
+    for name, kw in (("alibi", dict(alibi_slopes=slopes)), ("softcap50", dict(softcap=50.0))):
+        med, _ = timed(torch, np, lambda: b.attn_fwd(q, k, v, softmax_scale=w["scale"], causal=True,
+                                                     window=(4096, 0), out=oo, lse=ll, **kw), 5)
+        ex["long_local_s16384_w4096_" + name] = {
+            "ms": round(med, 4), "tflops": round(fl / (med * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, oo, ll
+
+    # packed-document block-sparse mask: B=2, H=16, S=8192, D=64
+    w = inputs.doc_mask()
+    q, k, v = to_dev(w["q"]), to_dev(w["k"]), to_dev(w["v"])
+    doc = torch.from_numpy(w["doc"]).to(dev)
+    med_m, _ = timed(torch, np, lambda: b.block_mask_build(2, 8192, 8192, 128, 128, causal=True,
+                                                            doc_q=doc, doc_k=doc), 10)
+    m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
+    oo = torch.empty_like(q)
+    ll = torch.empty((2, 16, 8192), dtype=torch.float32, device=dev)
+    med, _ = timed(torch, np, lambda: b.attn_fwd(q, k, v, softmax_scale=w["scale"], block_mask=m,
+                                                 out=oo, lse=ll), 10)
+    pairs = sum(n * (n + 1) // 2 for lens_b in w["doc_lengths"] for n in lens_b)
+    fl = 4.0 * 16 * 64 * pairs
+    ex["doc_mask_s8192_d64"] = {"block_mask_build_ms": round(med_m, 4), "fwd_ms": round(med, 4),
+                                "tflops": round(fl / (med * 1e-3) / 1e12, 2),
+                                "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 /
+                                                           PEAK_BF16_TFLOPS, 4)}
+    return ex
+
+
+def cpu_baseline(w, step_flops):
+    """The fp64 oracle (as it stands) on one full fwd + bwd step of the same
+    workload, on this host's cores."""
+    sys.path.insert(0, ROOT)
+    import oracle
+    from exact_attention_10_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        threads = len(os.sched_getaffinity(0))
+    q, k, v, do = (inputs.as_f64(w[n], "bf16") for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    oracle.attention_fwd(q, k, v, scale=w["scale"], causal=True)
+    oracle.attention_bwd(q, k, v, do, scale=w["scale"], causal=True)
+    dt = time.perf_counter() - t0
+    return {"value": round(step_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "one full fwd+bwd step of the B=1 Hq=32 Hkv=8 S=2048 D=128 causal "
+                      "workload, fp64 numpy (BLAS threads = cores)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -87,6 +87,11 @@ _lib.attn_bwd.restype = ctypes.c_int
 _lib.attn_bwd.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor, attn_tensor,
                           attn_tensor, ctypes.c_void_p, attn_tensor, attn_tensor, attn_tensor,
                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+_lib.attn_bwd_stage.restype = ctypes.c_int
+_lib.attn_bwd_stage.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor,
+                                attn_tensor, attn_tensor, ctypes.c_void_p, attn_tensor,
+                                attn_tensor, attn_tensor, ctypes.c_int32, ctypes.c_void_p,
+                                ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
 _lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
 _lib.attn_bwd_workspace_size.argtypes = [_P(attn_params)]
 _lib.attn_decode.restype = ctypes.c_int
@@ -104,7 +109,7 @@ _lib.block_mask_build.argtypes = [_P(attn_mask_desc), ctypes.c_int32, ctypes.c_i
                                   ctypes.c_void_p]
 
 EXPORTED = ["attn_status_string", "attn_last_error", "attn_fwd", "attn_fwd_tile_shape",
-            "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+            "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_size", "attn_decode",
             "attn_decode_workspace_size", "attn_block_mask_bytes", "block_mask_build"]
 
 
@@ -258,6 +263,17 @@ def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, window=(
                          1 if deterministic else 0, _ptr(workspace), workspace.numel(),
                          _stream()))
     return dq, dk, dv
+
+
+def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softmax_scale=None,
+                   causal=False, window=(-1, -1), alibi_slopes=None, softcap=0.0):
+    """Enqueue one stage (0 Delta, 1 dK/dV, 2 group sum, 3 dQ) of attn_bwd;
+    stages 0..3 in order with one workspace equal attn_bwd."""
+    D = q.shape[3]
+    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, None)
+    _check(_lib.attn_bwd_stage(ctypes.byref(p), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
+                               _tensor(dout), _ptr(lse), _tensor(dq), _tensor(dk), _tensor(dv), 1,
+                               _ptr(workspace), workspace.numel(), int(stage), _stream()))
 
 
 def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=0.0,

@@ -224,10 +224,10 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
   return hip_status(e, "attn_fwd launch");
 }
 
-attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_tensor v,
-                     attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
-                     attn_tensor dk, attn_tensor dv, int32_t deterministic, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                            attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
+                            attn_tensor dk, attn_tensor dv, int32_t deterministic, void* workspace,
+                            size_t workspace_bytes, int stage_mask, void* stream) {
   g_err[0] = 0;
   Common cm;
   attn_status st = check_params(p, &cm);
@@ -277,7 +277,26 @@ attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
   const size_t part = up((size_t)p->B * p->Sk * p->Hq * p->D * sizeof(float));
   a.part_dk = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest) : nullptr;
   a.part_dv = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest + part) : nullptr;
-  return hip_status(attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+  return hip_status(attn::launch_bwd_bf16(a, stage_mask, static_cast<hipStream_t>(stream)), "attn_bwd launch");
+}
+
+attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                     attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
+                     attn_tensor dk, attn_tensor dv, int32_t deterministic, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, q, k, v, o, dout, lse, dq, dk, dv, deterministic, workspace, workspace_bytes,
+                  attn::kBwdAllStages, stream);
+}
+
+attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k, attn_tensor v,
+                           attn_tensor o, attn_tensor dout, const float* lse, attn_tensor dq,
+                           attn_tensor dk, attn_tensor dv, int32_t deterministic,
+                           void* workspace, size_t workspace_bytes, int32_t stage,
+                           void* stream) {
+  g_err[0] = 0;
+  if (stage < 0 || stage > 3) return fail(ATTN_ERR_INVALID_ARG, "stage %d is not in 0..3", stage);
+  return bwd_impl(p, q, k, v, o, dout, lse, dq, dk, dv, deterministic, workspace, workspace_bytes,
+                  1 << stage, stream);
 }
 
 size_t attn_bwd_workspace_size(const attn_params* p) {

@@ -557,42 +557,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, int MOD>
-hipError_t launch_mod(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int partial = G > 1 ? 1 : 0;
   const int nkt = (a.Sk + KVCfg<D>::BN - 1) / KVCfg<D>::BN;
-  if (nkt > 0) {
+  if ((stages & 2) && nkt > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, MOD>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (partial && a.Sk > 0) {
-      const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * D;
-      hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((n + 255) / 256), dim3(256), 0, s, a);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+  }
+  if ((stages & 4) && partial && a.Sk > 0) {
+    const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * D;
+    hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   const int nqt = (a.Sq + QCfg<D>::BM - 1) / QCfg<D>::BM;
-  if (nqt == 0) return hipSuccess;
+  if (!(stages & 8) || nqt == 0) return hipSuccess;
   hipLaunchKernelGGL((bwd_dq_kernel<D, MOD>), dim3(nqt * a.Hq * a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
   constexpr int LPR = D / 8;
-  if (rows > 0) {
+  if ((stages & 1) && rows > 0) {
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((rows * LPR + 255) / 256), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0);
   switch (mod) {
-    case 0: return launch_mod<D, 0>(a, s);
-    case 1: return launch_mod<D, 1>(a, s);
-    case 2: return launch_mod<D, 2>(a, s);
-    default: return launch_mod<D, 3>(a, s);
+    case 0: return launch_mod<D, 0>(a, stages, s);
+    case 1: return launch_mod<D, 1>(a, stages, s);
+    case 2: return launch_mod<D, 2>(a, stages, s);
+    default: return launch_mod<D, 3>(a, stages, s);
   }
 }
 
@@ -605,10 +605,10 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   return n;
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stage_mask, hipStream_t s) {
   if (a.B == 0 || a.Hq == 0) return hipSuccess;
-  if (a.D == 64) return launch_d<64>(a, s);
-  return launch_d<128>(a, s);
+  if (a.D == 64) return launch_d<64>(a, stage_mask, s);
+  return launch_d<128>(a, stage_mask, s);
 }
 
 }  // namespace attn

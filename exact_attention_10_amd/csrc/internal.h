@@ -76,7 +76,9 @@ struct BwdArgs {
   float* part_dv;
 };
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+// stage_mask bit k runs stage k (0 Delta, 1 dK/dV, 2 group sum, 3 dQ).
+constexpr int kBwdAllStages = 0xF;
+hipError_t launch_bwd_bf16(const BwdArgs& a, int stage_mask, hipStream_t s);
 
 struct DecodeArgs {
   const void* q; const void* k; const void* v; void* o;

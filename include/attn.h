@@ -198,6 +198,23 @@ attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k,
                      size_t workspace_bytes, void* stream);
 size_t attn_bwd_workspace_size(const attn_params* p);
 
+/* One stage of attn_bwd, same arguments and workspace, for callers that
+ * time or interleave the stages.  Enqueuing stages 0, 1, 2, 3 in order on one
+ * stream (with the same workspace) is exactly attn_bwd:
+ *   0  Delta_i = <dout_i, o_i> into the workspace
+ *   1  dK/dV kernel (fp32 per-head partials in the workspace when Hq > Hkv,
+ *      else dk/dv directly)
+ *   2  sum of the per-head partials of each kv head into dk/dv, in head order
+ *      (nothing to do when Hq == Hkv)
+ *   3  dQ kernel (reads Delta)
+ * Errors: as attn_bwd; INVALID_ARG for a stage outside 0..3. */
+attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
+                           attn_tensor v, attn_tensor o, attn_tensor dout,
+                           const float* lse, attn_tensor dq, attn_tensor dk,
+                           attn_tensor dv, int32_t deterministic,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t stage, void* stream);
+
 /* ---------------------------------------------------------------------
  * Decode over a KV cache ([FA] flash_attn_with_kvcache: q attends to the
  * first cache_seqlens[b] rows of its batch row of k_cache / v_cache; no
