@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     // as the forward's tile classification, for this wave's 32 keys.
     const TileRange tr_q(win, qt, C::BM, 32);
     const int kt32 = kv0 / 32;
-    const bool full = tr_q.full(win, kt32, C::BM, 32);
+    const bool full = tr_q.full(kt32);
     const bool any = kt32 >= tr_q.kt_begin && kt32 < tr_q.kt_end;
 
     if (any) {
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int kt = range.kt_begin + t;
-    const bool full = range.full(win, kt, C::BM, C::BN);
+    const bool full = range.full(kt);
     const bool has_next = t + 1 < ntiles;
     if (has_next) load_regs(kt + 1);
 

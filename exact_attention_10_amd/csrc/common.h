@@ -63,6 +63,48 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// LDS image of a 64-row x D bf16 tile written by direct global->LDS loads.
+// A global_load_lds_dwordx4 instruction stores 16 bytes per lane at
+// consecutive 16-byte slots of a wave-uniform LDS base, so one instruction
+// fills a 1 KB "group" of RG = 512 / D rows.  Inside a group the slots are
+// chunk-major (slot = chunk * RG + row % RG) and groups are GS bytes apart.
+// With that layout 16 consecutive rows at one 16-byte chunk (a K fragment
+// read) fall in 16 different 4-bank groups, and the transposed reads of 4
+// consecutive rows x 32 columns touch 256 contiguous bytes.
+template <int D>
+struct TileLayout {
+  static constexpr int RG = 512 / D;                      // rows per group
+  static constexpr int CH = D / 8;                        // 16-byte chunks per row
+  static constexpr int GS = 1024 + (D == 128 ? 64 : 128); // group stride (bytes)
+  static constexpr int BYTES = (64 / RG) * GS;            // one 64-row tile
+  __device__ static constexpr int off(int row, int chunk) {
+    return (row / RG) * GS + (chunk * RG + row % RG) * 16;
+  }
+};
+
+// Wave-cooperative copy of rows [row0, row0 + 64) of a [rows, D] bf16 matrix
+// (row stride `ld` elements) into a TileLayout image at `tile`.  Rows at or
+// past `nrows` are read from row nrows - 1 instead (callers mask them), so no
+// address leaves the matrix.  4 waves; wave w copies groups w, w + 4, ...
+template <int D>
+__device__ __forceinline__ void tile_dma(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
+                                         int nrows, int wave, int lane) {
+  using L = TileLayout<D>;
+#pragma unroll
+  for (int u = 0; u < 64 / L::RG / 4; ++u) {
+    const int grp = wave + 4 * u;
+    const int row = grp * L::RG + lane % L::RG;
+    const int chunk = lane / L::RG;
+    int key = row0 + row;
+    key = key < nrows ? key : nrows - 1;
+    const bf16_t* gp = src + (int64_t)key * ld + chunk * 8;
+    bf16_t* lp = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(tile) + grp * L::GS);
+    __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Per-row allowed key interval for causal / sliding-window masks.
 // With delta = Sk - Sq, row i may attend keys j with
 //   lo(i) = max(0, i + delta - L) <= j <= hi(i) = min(Sk - 1, i + delta + R)
@@ -100,7 +142,8 @@ struct RowWindow {
 // block and the key tile are wholly in bounds, every row is non-empty and
 // every row's interval covers the tile; otherwise it is PARTIAL.
 struct TileRange {
-  int kt_begin, kt_end;
+  int kt_begin, kt_end;   // non-empty key tiles
+  int f_begin, f_end;     // FULL key tiles (a sub-range; empty when f_begin >= f_end)
   int r0, r1, i_first, i_last;
   __host__ __device__ TileRange(const RowWindow& w, int qt, int bm, int bn) {
     r0 = qt * bm;
@@ -109,20 +152,34 @@ struct TileRange {
     i_last = r1;
     if (w.R != kUnbounded) i_first = max(i_first, -w.delta - w.R);
     if (w.L != kUnbounded) i_last = min(i_last, w.Sk - 1 - w.delta + w.L);
-    kt_begin = 0;
-    kt_end = 0;
+    kt_begin = kt_end = f_begin = f_end = 0;
     if (w.Sk <= 0 || i_first > i_last) return;
-    int kmin = w.lo(i_first), kmax = w.hi(i_last);
+    const int kmin = w.lo(i_first), kmax = w.hi(i_last);
     if (kmax < kmin) return;
     kt_begin = kmin / bn;
     kt_end = kmax / bn + 1;
+    // FULL: the row block and key tile lie inside the matrix, no row is
+    // empty, and every row's interval covers the tile.  lo() grows with the
+    // row, so the binding rows are r1 for the lower and r0 for the upper end.
+    if (r0 + bm > w.Sq || i_first != r0 || i_last != r1) return;
+    const int lo_max = w.lo(r1), hi_min = w.hi(r0);
+    const int fb = (lo_max + bn - 1) / bn;
+    int fe = (hi_min + 1) / bn;                 // tiles with (kt + 1) * bn - 1 <= hi_min
+    if (fe > w.Sk / bn) fe = w.Sk / bn;         // and (kt + 1) * bn <= Sk
+    f_begin = max(fb, kt_begin);
+    f_end = min(fe, kt_end);
+    if (f_end < f_begin) f_end = f_begin;
   }
-  __host__ __device__ bool full(const RowWindow& w, int kt, int bm, int bn) const {
-    if (r0 + bm > w.Sq || (kt + 1) * bn > w.Sk) return false;
-    if (i_first != r0 || i_last != r1) return false;
-    if (w.lo(r1) > kt * bn) return false;
-    if (w.hi(r0) < (kt + 1) * bn - 1) return false;
-    return true;
+  __host__ __device__ bool full(int kt) const { return kt >= f_begin && kt < f_end; }
+  __host__ __device__ int n_full() const { return f_end - f_begin; }
+  // The t-th tile when FULL tiles come first, then the partial ones in
+  // ascending order.
+  __host__ __device__ int kt_at(int t) const {
+    const int nf = f_end - f_begin;
+    if (t < nf) return f_begin + t;
+    const int p = t - nf;
+    const int before = f_begin - kt_begin;
+    return p < before ? kt_begin + p : f_end + (p - before);
   }
 };
 

@@ -28,6 +28,8 @@
 // the maximum in use, so p = exp2(x - m_used) <= 256.  Sum and output use the
 // same m_used, so the final O = acc / l and LSE = m_used + log2(l) are exact.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -42,11 +44,8 @@ struct FwdCfg {
   static constexpr int BM = kFwdBM;        // query rows per workgroup
   static constexpr int BN = kFwdBN;        // keys per tile
   static constexpr int NT = 256;           // threads (4 waves)
-  static constexpr int KS = D + 8;         // K row stride in LDS (elements)
-  static constexpr int VS = D + 32;        // V row stride in LDS (elements)
-  static constexpr int KT = BN * KS;       // elements per K buffer
-  static constexpr int VT = BN * VS;       // elements per V buffer
-  static constexpr int CPT = BN * D / 8 / NT;  // 16-byte chunks per thread
+  using L = TileLayout<D>;                 // LDS image of a 64-key K or V tile
+  static constexpr int TB = L::BYTES;      // bytes per tile buffer
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
 };
@@ -60,19 +59,170 @@ __device__ __forceinline__ bf16x8 zero_frag() {
   return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 }
 
+struct TileCtx {
+  float scale_log2;   // |scale| * log2(e)
+  float slope_log2;   // ALiBi slope * log2(e)
+  float cap_k2;       // 2 log2(e) |scale| / softcap
+  float cap_log2;     // softcap * log2(e)
+  int qpos;           // query row + (Sk - Sq): position compared with keys
+  int row_lo;         // first allowed key of this lane's row
+  int row_span;       // number of allowed keys from row_lo (0: empty row)
+  int doc;            // document id of this lane's row
+  bool has_doc;
+};
+
+// Key offset (within a 64-key tile, relative to 4*g) of S^T register r of
+// 32-key half kb: rows 8*(r/4) + r%4 of the 32x32 accumulator.
+__device__ __forceinline__ constexpr int koff(int kb, int r) { return 32 * kb + 8 * (r >> 2) + (r & 3); }
+
+// One 64-key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
+// MASKED evaluates the mask predicate per element (partial tiles only).
+template <int D, int MOD, bool MASKED>
+__device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_base,
+                                         const int* doc_t, const bf16x8 (&qf)[D / 16],
+                                         f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                         const TileCtx& cx, int key_base, int lane) {
+  using C = FwdCfg<D>;
+  constexpr bool kAlibi = MOD & 1;
+  constexpr bool kSoftcap = MOD & 2;
+  constexpr bool kScaled = kAlibi || kSoftcap;
+  const int g = lane >> 5, c = lane & 31;
+
+  // S^T for the two 32-key halves.  The two accumulators are updated in
+  // alternation so consecutive MFMAs never depend on each other (a dependent
+  // accumulation waits for the previous MFMA to drain).
+  f32x16 sacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ds += 2) {
+    bf16x8 ka[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        ka[kb][u] = *reinterpret_cast<const bf16x8*>(kb_base + C::L::off(32 * kb + c, 2 * (ds + u) + g));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[kb][u], qf[ds + u], sacc[kb]);
+  }
+
+  // Scores in the exp2 domain (raw dot products when no modifier: the
+  // positive scale is then applied inside the exponent).
+  if (kScaled) {
+    const float dist_base = static_cast<float>(cx.qpos - key_base - 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x;
+        if (kSoftcap) {
+          // softcap * tanh(scale * s / softcap); tanh(y) = 1 - 2 / (e^{2y} + 1)
+          const float e = fast_exp2(sacc[kb][r] * cx.cap_k2);
+          x = cx.cap_log2 * (1.0f - 2.0f * fast_rcp(e + 1.0f));
+        } else {
+          x = sacc[kb][r] * cx.scale_log2;
+        }
+        if (kAlibi)
+          x = __builtin_fmaf(-cx.slope_log2, fabsf(dist_base - static_cast<float>(koff(kb, r))), x);
+        sacc[kb][r] = x;
+      }
+  }
+  if (MASKED) {
+    // allowed <=> 0 <= key - row_lo < row_span (unsigned compare), and the
+    // same document when a document mask is given.
+    const uint32_t span = static_cast<uint32_t>(cx.row_span);
+    const int jb = key_base + 4 * g - cx.row_lo;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        int4 dk = make_int4(0, 0, 0, 0);
+        if (cx.has_doc) dk = *reinterpret_cast<const int4*>(doc_t + 4 * g + 32 * kb + 8 * rr);
+        const int dks[4] = {dk.x, dk.y, dk.z, dk.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          bool ok = static_cast<uint32_t>(jb + koff(kb, r)) < span;
+          if (cx.has_doc) ok = ok && dks[e] == cx.doc;
+          sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+        }
+      }
+  }
+
+  // Row maximum: tree over this lane's 32 values, then lane l ^ 32.
+  float m4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    m4[i] = fmaxf(fmaxf(fmaxf(sacc[0][i], sacc[0][i + 4]), fmaxf(sacc[0][i + 8], sacc[0][i + 12])),
+                  fmaxf(fmaxf(sacc[1][i], sacc[1][i + 4]), fmaxf(sacc[1][i + 8], sacc[1][i + 12])));
+  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  mx = fmaxf(mx, wave_xor32(mx));
+  const float mx2 = kScaled ? mx : mx * cx.scale_log2;  // -inf stays -inf
+  if (__any(mx2 > m_run + kRescaleThreshold)) {
+    const float m_new = fmaxf(m_run, mx2);
+    const float alpha = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+  }
+  const float msub = (m_run == kNegInf) ? 0.0f : m_run;
+
+  // P = exp2(x - m), packed to bf16 as the B operand of O^T += V^T P^T.
+  bf16x8 pf[2][2];
+  float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = kScaled ? fast_exp2(sacc[kb][r] - msub)
+                              : fast_exp2(__builtin_fmaf(sacc[kb][r], cx.scale_log2, -msub));
+      ls[r & 3] += p;
+      pf[kb][r >> 3][r & 7] = static_cast<__bf16>(p);
+    }
+  l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+  // O^T += V^T P^T; V^T fragments by transposed LDS reads.  For each
+  // 16-key step the D/32 output blocks are independent accumulators, issued
+  // back to back.
+  const int beta = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
+  const int tr_chunk = 2 * (beta & 1) + ((s16 & 3) >> 1);
+  const int tr_half = 8 * (s16 & 1);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 va[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) {
+      const char* p0 = vb_base + C::L::off(16 * kk + tr_row, 4 * db + tr_chunk) + tr_half;
+      const char* p1 = vb_base + C::L::off(16 * kk + 8 + tr_row, 4 * db + tr_chunk) + tr_half;
+      va[db] = cat_frag(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+                        lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
+    }
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) oacc[db] = mfma32(va[db], pf[kk >> 1][kk & 1], oacc[db]);
+  }
+}
+
 template <int D, int MOD>  // MOD bit 0: ALiBi, bit 1: softcap
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
 
-  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * C::KT];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * C::VT];
+  __shared__ __attribute__((aligned(16))) char lds_k[2 * C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_v[2 * C::TB];
   __shared__ int lds_doc[2 * C::BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;   // k-group of the MFMA operands
   const int c = lane & 31;   // column (query) of S^T / O^T
 
@@ -138,11 +288,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   } else {
     ntiles = range.kt_end - range.kt_begin;
   }
+  // Tiles in processing order: all FULL tiles first, then the PARTIAL ones.
+  const int nfull_tiles = sparse ? n_full * a.tiles.sub : range.n_full();
   auto tile_at = [&](int t) -> Tile {
     Tile r;
     if (!sparse) {
-      r.kt = range.kt_begin + t;
-      r.full = range.full(win, r.kt, C::BM, C::BN);
+      r.kt = range.kt_at(t);
+      r.full = t < nfull_tiles;
     } else {
       const int mt = t / a.tiles.sub, sb = t % a.tiles.sub;
       if (mt < n_full) {
@@ -160,37 +312,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int doc_mine = (has_doc && q_ok) ? a.mask.doc_q[(int64_t)b * a.Sq + my_q] : 0;
   const int delta = a.Sk - a.Sq;
 
-  uint4 kr[C::CPT], vr[C::CPT];
   int doc_r = 0;
-  auto load_regs = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int row = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      const int key = kt * C::BN + row;
-      if (key < a.Sk) {
-        kr[u] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * a.k_ss + col);
-        vr[u] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * a.v_ss + col);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  // K and V of tile kt into buffer buf (direct global->LDS), and this
+  // thread's document id of the tile into a register.
+  auto load_tile = [&](int kt, int buf) {
+    tile_dma<D>(reinterpret_cast<bf16_t*>(lds_k + buf * C::TB), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(lds_v + buf * C::TB), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
     if (has_doc && tid < C::BN) {
       const int key = kt * C::BN + tid;
       doc_r = key < a.Sk ? a.mask.doc_k[(int64_t)b * a.Sk + key] : -1;
     }
   };
-  auto store_regs = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int row = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(lds_k + buf * C::KT + row * C::KS + col) = kr[u];
-      *reinterpret_cast<uint4*>(lds_v + buf * C::VT + row * C::VS + col) = vr[u];
-    }
+  auto store_doc = [&](int buf) {
     if (has_doc && tid < C::BN) lds_doc[buf * C::BN + tid] = doc_r;
   };
 
@@ -207,144 +340,43 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
   if (ntiles > 0) {
-    load_regs(tile_at(0).kt);
-    store_regs(0);
+    load_tile(tile_at(0).kt, 0);
+    store_doc(0);
   }
+  wait_dma();
   __syncthreads();
 
-  // V^T transposed-read coordinates of this lane (see lds_read_tr16).
-  const int beta = lane >> 4, s16 = lane & 15;
-  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
-  const int tr_col = 16 * (beta & 1) + 4 * (s16 & 3);
+  // Per-row allowed key interval [lo, lo + span) for partial tiles; an empty
+  // row (or a row past Sq) has span 0.
+  int row_lo = 0, row_span = 0;
+  if (q_ok && win.row_nonempty(my_q)) {
+    row_lo = win.lo(my_q);
+    row_span = win.hi(my_q) - row_lo + 1;
+  }
+  const TileCtx ctx{scale_log2, slope_log2, cap_k2, cap_log2, my_q + delta, row_lo, row_span,
+                    doc_mine, has_doc};
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One loop per tile kind, so each loop body is a single instantiation and
+  // the accumulators keep their registers across iterations.
+  auto step = [&](int t, auto masked) {
     const int buf = t & 1;
     const Tile cur = tile_at(t);
     const bool has_next = t + 1 < ntiles;
-    if (has_next) load_regs(tile_at(t + 1).kt);
-
+    if (has_next) load_tile(tile_at(t + 1).kt, buf ^ 1);
     if (trace_row != nullptr) {
       if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
       else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
     }
-
-    // ---- S^T = K Q^T (64 keys x 32 queries per wave)
-    const bf16_t* kb_base = lds_k + buf * C::KT;
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb_base + (32 * kb + c) * C::KS + 16 * ds + 8 * g);
-        sacc[kb] = mfma32(ka, qf[ds], sacc[kb]);
-      }
-    }
-
-    // ---- scores in the exp2 domain.  Without modifiers the values stay raw
-    // dot products (the positive scale is applied inside the exponent).
-    constexpr bool kScaled = kAlibi || kSoftcap;
-    const int key0 = cur.kt * C::BN + 4 * g;  // key of register r is key0 + koff(kb, r)
-    if (kScaled) {
-      const float dist_base = static_cast<float>(my_q + delta - key0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = sacc[kb][r];
-          float x;
-          if (kSoftcap) {
-            // c * tanh(scale * s / c) in exp2 units; tanh(y) = 1 - 2 / (e^{2y} + 1)
-            const float e = fast_exp2(s * cap_k2);
-            x = cap_log2 * (1.0f - 2.0f * fast_rcp(e + 1.0f));
-          } else {
-            x = s * scale_log2;
-          }
-          if (kAlibi) {
-            const float koff = static_cast<float>(32 * kb + 8 * (r >> 2) + (r & 3));
-            x = __builtin_fmaf(-slope_log2, fabsf(dist_base - koff), x);
-          }
-          sacc[kb][r] = x;
-        }
-      }
-    }
-    if (!cur.full) {
-      const int* doc_t = lds_doc + buf * C::BN;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int koff = 32 * kb + 8 * (r >> 2) + (r & 3);
-          const int j = key0 + koff;
-          const int i = my_q + delta;  // bottom-right aligned row position
-          bool ok = q_ok && j < a.Sk;
-          if (a.mask.causal) ok = ok && j <= i;
-          if (a.mask.wl >= 0) ok = ok && j >= i - a.mask.wl;
-          if (a.mask.wr >= 0) ok = ok && j <= i + a.mask.wr;
-          if (has_doc) ok = ok && doc_t[4 * g + koff] == doc_mine;
-          if (!ok) sacc[kb][r] = kNegInf;
-        }
-      }
-    }
-
-    // ---- online softmax
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float mx2 = kScaled ? mx : mx * scale_log2;  // -inf stays -inf
-    const bool need = mx2 > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float m_new = fmaxf(m_run, mx2);
-      const float alpha = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
-    }
-    const float msub = (m_run == kNegInf) ? 0.0f : m_run;
-
-    bf16x8 pf[2][2];
-    float ls = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = kScaled ? fast_exp2(sacc[kb][r] - msub)
-                                : fast_exp2(__builtin_fmaf(sacc[kb][r], scale_log2, -msub));
-        ls += p;
-        pf[kb][r >> 3][r & 7] = static_cast<__bf16>(p);
-      }
-    }
-    l_run += ls;
-
-    // ---- O^T += V^T P^T
-    const bf16_t* vb_base = lds_v + buf * C::VT;
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16_t* p0 = vb_base + (32 * kb + 16 * ks + tr_row) * C::VS + 32 * db + tr_col;
-          const i16x4 lo = lds_read_tr16(p0);
-          const i16x4 hi = lds_read_tr16(p0 + 8 * C::VS);
-          const bf16x8 va = cat_frag(lo, hi);
-          oacc[db] = mfma32(va, pf[kb][ks], oacc[db]);
-        }
-      }
-    }
-
-    if (has_next) store_regs(buf ^ 1);
+    fwd_tile<D, MOD, decltype(masked)::value>(lds_k + buf * C::TB, lds_v + buf * C::TB,
+                                              lds_doc + buf * C::BN, qf, oacc, m_run, l_run, ctx,
+                                              cur.kt * C::BN, lane);
+    if (has_next) store_doc(buf ^ 1);
+    wait_dma();
     __syncthreads();
-  }
+  };
+  int t = 0;
+  for (; t < nfull_tiles; ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + wave_xor32(l_run);

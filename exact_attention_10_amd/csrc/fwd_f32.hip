@@ -65,7 +65,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
     bool full;
     if (!sparse) {
       kt = range.kt_begin + t;
-      full = range.full(win, kt, BM, BN);
+      full = range.full(kt);
     } else {
       const int mt = t / a.tiles.sub, sb = t % a.tiles.sub;
       const int64_t base = (int64_t)mrow * a.tiles.nK;
