@@ -224,8 +224,10 @@ def _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block
     return p
 
 
-def tile_shape(q, k, block_mask=None):
-    p = _params(q, k, q.shape[3], None, False, (-1, -1), None, 0.0, block_mask)
+def tile_shape(q, k, block_mask=None, causal=False):
+    """(rows, keys) of the forward's tiles for this problem: the tile trace
+    has ceil(Sq / rows) x ceil(Sk / keys) entries per (batch, head)."""
+    p = _params(q, k, q.shape[3], None, causal, (-1, -1), None, 0.0, block_mask)
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     _check(_lib.attn_fwd_tile_shape(ctypes.byref(p), _dtype_code(q), ctypes.byref(bm),
                                     ctypes.byref(bn)))

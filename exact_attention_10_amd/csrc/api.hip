@@ -160,7 +160,7 @@ attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype, int32_t* bl
     *block_m = p->block_mask->block_m;
     *block_n = p->block_mask->block_n;
   } else if (dtype == ATTN_BF16) {
-    *block_m = attn::kFwdBM;
+    *block_m = attn::fwd_bf16_rows_per_block(p->B, p->Sq, p->Hq, p->causal, false);
     *block_n = attn::kFwdBN;
   } else {
     *block_m = attn::kFwdF32BM;
@@ -214,7 +214,8 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
     a.nQt = bm->nQ;
     a.nKt = bm->nK;
   } else {
-    const int bmr = dt == ATTN_BF16 ? attn::kFwdBM : attn::kFwdF32BM;
+    const int bmr = dt == ATTN_BF16 ? attn::fwd_bf16_rows_per_block(p->B, p->Sq, p->Hq, p->causal, false)
+                                    : attn::kFwdF32BM;
     const int bnr = dt == ATTN_BF16 ? attn::kFwdBN : attn::kFwdF32BN;
     a.nQt = (p->Sq + bmr - 1) / bmr;
     a.nKt = (p->Sk + bnr - 1) / bnr;

@@ -85,14 +85,15 @@ struct TileLayout {
 // Wave-cooperative copy of rows [row0, row0 + 64) of a [rows, D] bf16 matrix
 // (row stride `ld` elements) into a TileLayout image at `tile`.  Rows at or
 // past `nrows` are read from row nrows - 1 instead (callers mask them), so no
-// address leaves the matrix.  4 waves; wave w copies groups w, w + 4, ...
-template <int D>
+// address leaves the matrix.  NW waves; wave w copies groups w, w + NW, ...
+template <int D, int NW = 4>
 __device__ __forceinline__ void tile_dma(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
                                          int nrows, int wave, int lane) {
   using L = TileLayout<D>;
+  static_assert((64 / L::RG) % NW == 0, "groups must divide among the waves");
 #pragma unroll
-  for (int u = 0; u < 64 / L::RG / 4; ++u) {
-    const int grp = wave + 4 * u;
+  for (int u = 0; u < 64 / L::RG / NW; ++u) {
+    const int grp = wave + NW * u;
     const int row = grp * L::RG + lane % L::RG;
     const int chunk = lane / L::RG;
     int key = row0 + row;

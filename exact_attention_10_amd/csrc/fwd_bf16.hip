@@ -39,11 +39,11 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D>
+template <int D, int NW = 4>
 struct FwdCfg {
-  static constexpr int BM = kFwdBM;        // query rows per workgroup
+  static constexpr int BM = 32 * NW;       // query rows per workgroup (32 per wave)
   static constexpr int BN = kFwdBN;        // keys per tile
-  static constexpr int NT = 256;           // threads (4 waves)
+  static constexpr int NT = 64 * NW;       // threads
   using L = TileLayout<D>;                 // LDS image of a 64-key K or V tile
   static constexpr int TB = L::BYTES;      // bytes per tile buffer
   static constexpr int DSTEPS = D / 16;
@@ -210,15 +210,25 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
   }
 }
 
-template <int D, int MOD>  // MOD bit 0: ALiBi, bit 1: softcap
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
-  using C = FwdCfg<D>;
+// NW waves of 32 query rows: 4 (128 rows, two workgroups per CU) or 8 (256
+// rows, one workgroup per CU; each K/V tile copied to LDS feeds twice the
+// query rows, halving the L2-to-LDS traffic per flop).
+template <int D, int MOD, int NW>  // MOD bit 0: ALiBi, bit 1: softcap
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D, NW>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
 
-  __shared__ __attribute__((aligned(16))) char lds_k[2 * C::TB];
-  __shared__ __attribute__((aligned(16))) char lds_v[2 * C::TB];
-  __shared__ int lds_doc[2 * C::BN];
+  // Two distinct LDS objects per operand (not one array indexed by the
+  // buffer): alias analysis can then see that the direct global->LDS copy of
+  // the next tile does not touch the buffer being read, and no wait for the
+  // copy is placed before the reads of the current tile.
+  __shared__ __attribute__((aligned(16))) char lds_k0[C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_k1[C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_v0[C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_v1[C::TB];
+  __shared__ int lds_doc0[C::BN];
+  __shared__ int lds_doc1[C::BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -313,19 +323,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int delta = a.Sk - a.Sq;
 
   int doc_r = 0;
-  // K and V of tile kt into buffer buf (direct global->LDS), and this
+  // K and V of tile kt into buffer BUF (direct global->LDS), and this
   // thread's document id of the tile into a register.
-  auto load_tile = [&](int kt, int buf) {
-    tile_dma<D>(reinterpret_cast<bf16_t*>(lds_k + buf * C::TB), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
-    tile_dma<D>(reinterpret_cast<bf16_t*>(lds_v + buf * C::TB), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
+  auto load_tile = [&](int kt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    char* kdst = BUF ? lds_k1 : lds_k0;
+    char* vdst = BUF ? lds_v1 : lds_v0;
+    tile_dma<D, NW>(reinterpret_cast<bf16_t*>(kdst), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
+    tile_dma<D, NW>(reinterpret_cast<bf16_t*>(vdst), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
     if (has_doc && tid < C::BN) {
       const int key = kt * C::BN + tid;
       doc_r = key < a.Sk ? a.mask.doc_k[(int64_t)b * a.Sk + key] : -1;
     }
   };
-  auto store_doc = [&](int buf) {
-    if (has_doc && tid < C::BN) lds_doc[buf * C::BN + tid] = doc_r;
+  auto store_doc = [&](auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (has_doc && tid < C::BN) (BUF ? lds_doc1 : lds_doc0)[tid] = doc_r;
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   uint8_t* trace_row = nullptr;
   if (a.trace != nullptr && tid == 0)
@@ -340,8 +356,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
   if (ntiles > 0) {
-    load_tile(tile_at(0).kt, 0);
-    store_doc(0);
+    load_tile(tile_at(0).kt, B0{});
+    store_doc(B0{});
   }
   wait_dma();
   __syncthreads();
@@ -356,27 +372,41 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const TileCtx ctx{scale_log2, slope_log2, cap_k2, cap_log2, my_q + delta, row_lo, row_span,
                     doc_mine, has_doc};
 
-  // One loop per tile kind, so each loop body is a single instantiation and
-  // the accumulators keep their registers across iterations.
-  auto step = [&](int t, auto masked) {
-    const int buf = t & 1;
+  // Tile t lives in buffer t % 2.  Loops are unrolled by two so the buffer
+  // is a compile-time choice, and full and partial tiles have loops of their
+  // own, so each loop body is one instantiation and the accumulators keep
+  // their registers across iterations.
+  auto step = [&](int t, auto buf_tag, auto masked) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using NEXT = std::integral_constant<int, 1 - BUF>;
     const Tile cur = tile_at(t);
     const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(tile_at(t + 1).kt, buf ^ 1);
+    if (has_next) load_tile(tile_at(t + 1).kt, NEXT{});
     if (trace_row != nullptr) {
       if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
       else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
     }
-    fwd_tile<D, MOD, decltype(masked)::value>(lds_k + buf * C::TB, lds_v + buf * C::TB,
-                                              lds_doc + buf * C::BN, qf, oacc, m_run, l_run, ctx,
-                                              cur.kt * C::BN, lane);
-    if (has_next) store_doc(buf ^ 1);
+    fwd_tile<D, MOD, decltype(masked)::value>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
+                                              BUF ? lds_doc1 : lds_doc0, qf, oacc, m_run, l_run,
+                                              ctx, cur.kt * C::BN, lane);
+    if (has_next) store_doc(NEXT{});
     wait_dma();
     __syncthreads();
   };
+  using FULL = std::false_type;
+  using PART = std::true_type;
   int t = 0;
-  for (; t < nfull_tiles; ++t) step(t, std::false_type{});
-  for (; t < ntiles; ++t) step(t, std::true_type{});
+  for (; t + 1 < nfull_tiles; t += 2) {
+    step(t, B0{}, FULL{});
+    step(t + 1, B1{}, FULL{});
+  }
+  if (t < nfull_tiles) step(t++, B0{}, FULL{});
+  if (t < ntiles && (t & 1)) step(t++, B1{}, PART{});
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B0{}, PART{});
+    step(t + 1, B1{}, PART{});
+  }
+  if (t < ntiles) step(t++, B0{}, PART{});
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + wave_xor32(l_run);
@@ -400,26 +430,39 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, int NW>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-  const int nqt = (a.Sq + kFwdBM - 1) / kFwdBM;
-  const dim3 grid(nqt * a.Hq * a.B), block(256);
+  const int bm = 32 * NW;
+  const int nqt = (a.Sq + bm - 1) / bm;
+  const dim3 grid(nqt * a.Hq * a.B), block(64 * NW);
   const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0);
   switch (mod) {
-    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<D, 0>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, 3>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, NW>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, NW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, NW>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, 3, NW>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+int fwd_bf16_rows_per_block(int B, int Sq, int Hq, int causal, bool sparse) {
+  if (sparse) return 128;
+  const long wg256 = (long)((Sq + 255) / 256) * Hq * B;
+  // 256-row workgroups fill the GPU with one workgroup per CU; with causal
+  // masks per-tile work differs, so they are only used when there are enough
+  // tiles to even it out.
+  if (wg256 >= 256 && (!causal || wg256 >= 1024)) return 256;
+  return 128;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   if (a.Sq == 0 || a.B == 0 || a.Hq == 0) return hipSuccess;
-  if (a.D == 64) return launch_d<64>(a, s);
-  return launch_d<128>(a, s);
+  const bool sparse = a.tiles.kv_num_full != nullptr;
+  const bool wide = fwd_bf16_rows_per_block(a.B, a.Sq, a.Hq, a.mask.causal, sparse) == 256;
+  if (a.D == 64) return wide ? launch_d<64, 8>(a, s) : launch_d<64, 4>(a, s);
+  return wide ? launch_d<128, 8>(a, s) : launch_d<128, 4>(a, s);
 }
 
 }  // namespace attn

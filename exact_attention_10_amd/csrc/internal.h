@@ -43,9 +43,11 @@ struct FwdArgs {
   TileLists tiles;
 };
 
-// bf16 MFMA forward.  Tile 128 query rows x 64 keys.
+// bf16 MFMA forward.  Tiles of 128 or 256 query rows x 64 keys (block-sparse
+// masks use 128-row tiles).
 constexpr int kFwdBM = 128;
 constexpr int kFwdBN = 64;
+int fwd_bf16_rows_per_block(int B, int Sq, int Hq, int causal, bool sparse);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 
 // fp32 vector-ALU forward.  Tile 64 x 64.

@@ -27,12 +27,14 @@ def run_fwd(b, w, trace=False, **kw):
     v = to_device(w["v"], w["dtype"], torch)
     tr = None
     if trace:
-        bm, bn = b.tile_shape(q, k, kw.get("block_mask"))
+        bm, bn = b.tile_shape(q, k, kw.get("block_mask"), kw.get("causal", False))
         nq = -(-q.shape[1] // bm)
         nk = -(-k.shape[1] // bn)
         tr = torch.zeros((q.shape[0], q.shape[2], nq, nk), dtype=torch.uint8, device="cuda")
     o, lse = b.attn_fwd(q, k, v, tile_trace=tr, **kw)
     torch.cuda.synchronize()
+    if trace:
+        tr.tile = (bm, bn)
     return o, lse, tr
 
 
@@ -87,7 +89,7 @@ def test_fwd_bf16_parity_and_trace(b, case):
                                 alibi_slopes=slopes, softcap=kw["softcap"])
     check_o(to_f64(o), O)
     check_lse(to_f64(lse), L)
-    exp = expected_trace(B, Hq, Sq, Sk, 128, 64, kw["causal"], kw["window"])
+    exp = expected_trace(B, Hq, Sq, Sk, *tr.tile, kw["causal"], kw["window"])
     np.testing.assert_array_equal(tr.cpu().numpy(), exp)
 
 
@@ -134,7 +136,7 @@ def test_fwd_llama8b_causal_full(b):
     check_o(to_f64(o), O)
     check_lse(to_f64(lse), L)
     np.testing.assert_array_equal(tr.cpu().numpy(),
-                                  expected_trace(1, 32, 2048, 2048, 128, 64, True))
+                                  expected_trace(1, 32, 2048, 2048, *tr.tile, True))
     o2, lse2, _ = run_fwd(b, w, softmax_scale=w["scale"], causal=True)
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
@@ -168,7 +170,7 @@ def test_fwd_long_local_sampled(b, long_local, mod):
                                            softcap=kw.get("softcap", 0.0))
         check_o(o[0, rows, h], Or, what="O[h=%d]" % h)
         check_lse(lse[0, h, rows], Lr)
-    exp = expected_trace(1, 32, 16384, 16384, 128, 64, True, (4096, 0))
+    exp = expected_trace(1, 32, 16384, 16384, *tr.tile, True, (4096, 0))
     np.testing.assert_array_equal(tr.cpu().numpy(), exp)
 
 
@@ -236,3 +238,15 @@ def test_fwd_doc_block_sparse_small_full(b):
     check_lse(to_f64(lse), L)
     np.testing.assert_array_equal(tr.cpu().numpy(),
                                   expected_trace(2, 4, 300, 300, 128, 128, True, doc=w["doc"]))
+
+
+def test_fwd_wide_tiles_noncausal(b):
+    """A problem large enough for 256-row tiles (non-causal, 32 heads x 2048
+    rows): every output against the oracle, trace at the reported tile shape."""
+    w = inputs.random_case(77, 1, 2048, 1900, 32, 8, 128, dtype="bf16")
+    o, lse, tr = run_fwd(b, w, trace=True, softmax_scale=0.09)
+    assert tr.tile == (256, 64)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=0.09)
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    np.testing.assert_array_equal(tr.cpu().numpy(), expected_trace(1, 32, 2048, 1900, 256, 64))
