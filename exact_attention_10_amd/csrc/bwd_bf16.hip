@@ -28,6 +28,8 @@
 //     dP^T = V dO^T give one query per lane, and dQ^T += K^T dS^T uses
 //     transposed reads of the K tile.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -69,30 +71,39 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   if (row < rows && part == 0) a.delta[((int64_t)b * a.Hq + h) * a.Sq + i] = acc;
 }
 
-// Scores in the exp2 domain for a raw dot product r of (query i, key j).
-template <bool kAlibi, bool kSoftcap>
-__device__ __forceinline__ float score_x(float r, float scale_log2, float cap_k2, float cap_log2,
-                                         float slope_log2, int dist, float* tanh_out) {
-  float x;
-  if (kSoftcap) {
-    const float e = fast_exp2(r * cap_k2);
-    const float th = 1.0f - 2.0f * fast_rcp(e + 1.0f);
-    *tanh_out = th;
-    x = cap_log2 * th;
-  } else {
-    x = r * scale_log2;
-  }
-  if (kAlibi) x = __builtin_fmaf(-slope_log2, fabsf(static_cast<float>(dist)), x);
-  return x;
+struct BwdCtx {
+  float scale_log2;   // |scale| * log2(e)
+  float sgn;          // sign of the scale (applied to the raw dot product)
+  float slope_log2;   // ALiBi slope * log2(e)
+  float cap_k2;       // 2 log2(e) |scale| / softcap
+  float cap_log2;     // softcap * log2(e)
+  int delta_pos;      // Sk - Sq
+};
+
+// Key offset (within a 64-row tile, relative to 4*g) of accumulator
+// register r of 32-row block kb: rows 8*(r/4) + r%4 of a 32x32 MFMA result.
+__device__ __forceinline__ constexpr int roff(int kb, int r) { return 32 * kb + 8 * (r >> 2) + (r & 3); }
+
+// Transposed-read address (bytes) inside a TileLayout<D> image for the
+// 16-row step kk and 32-column block db: rows 16*kk + tr_row (and +8),
+// columns 32*db + tr_col .. +3 (see lds_read_tr16).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int kk, int db, int lane) {
+  using L = TileLayout<D>;
+  const int beta = lane >> 4, s16 = lane & 15;
+  const int row = 16 * kk + 4 * (beta >> 1) + (s16 >> 2);
+  const int chunk = 4 * db + 2 * (beta & 1) + ((s16 & 3) >> 1);
+  const int half = 8 * (s16 & 1);
+  const char* p0 = tile + L::off(row, chunk) + half;
+  const char* p1 = tile + L::off(row + 8, chunk) + half;
+  return cat_frag(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+                  lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
 }
 
-__device__ __forceinline__ bool mask_ok(const MaskArgs& m, int Sq, int Sk, int i, int j) {
-  if (i >= Sq || j >= Sk) return false;
-  const int ii = i + (Sk - Sq);
-  if (m.causal && j > ii) return false;
-  if (m.wl >= 0 && j < ii - m.wl) return false;
-  if (m.wr >= 0 && j > ii + m.wr) return false;
-  return true;
+// A-operand row read (16 bytes) of row `row`, d = 16*ds + 8*g .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int ds, int g) {
+  return *reinterpret_cast<const bf16x8*>(tile + TileLayout<D>::off(row, 2 * ds + g));
 }
 
 // ---------------------------------------------------------------------------
@@ -101,28 +112,137 @@ __device__ __forceinline__ bool mask_ok(const MaskArgs& m, int Sq, int Sk, int i
 template <int D>
 struct KVCfg {
   static constexpr int BN = 128;           // keys per workgroup (4 waves x 32)
-  static constexpr int BM = 32;            // queries per streamed tile
-  static constexpr int NT = 256;
-  static constexpr int QS = D + 16;        // LDS row stride of the Q / dO tiles
-  static constexpr int QT = BM * QS;
-  static constexpr int CPT = BM * D / 8 / NT;  // 16-byte chunks per thread (Q or dO)
+  static constexpr int BM = 64;            // queries per streamed tile
+  using L = TileLayout<D>;
+  static constexpr int TB = L::BYTES;
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
 };
 
+// One 64-query tile against this wave's 32 keys.  S = Q K^T and dP = dO V^T
+// give one key per lane (queries along the accumulator registers), so P and
+// dS rounded to bf16 are the A operands of dV += P^T dO and dK += dS^T Q.
 template <int D, int MOD>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial) {
+__device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_lds, const float* lse_t,
+                                          const float* dl_t, const bf16x8 (&kf)[D / 16],
+                                          const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
+                                          f32x16 (&dv)[D / 32], const BwdCtx& cx, int q0, int my_key,
+                                          bool masked, int rows_first, int rows_count, int lane) {
   using C = KVCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_q[2 * C::QT];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_do[2 * C::QT];
-  __shared__ __attribute__((aligned(16))) float lds_lse[2 * C::BM];
-  __shared__ __attribute__((aligned(16))) float lds_dl[2 * C::BM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, c = lane & 31;
-  const int nkt = (a.Sk + C::BN - 1) / C::BN;
+
+  f32x16 s[2], dp[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[qb][r] = 0.0f;
+      dp[qb][r] = 0.0f;
+    }
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    bf16x8 qa[2], da[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      qa[qb] = row_frag<D>(qt_lds, 32 * qb + c, ds, g);
+      da[qb] = row_frag<D>(dot_lds, 32 * qb + c, ds, g);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = mfma32(qa[qb], kf[ds], s[qb]);
+      dp[qb] = mfma32(da[qb], vf[ds], dp[qb]);
+    }
+  }
+
+  // P = exp2(x - lse2) and dS = P (dP - Delta) [* (1 - tanh^2)], in place.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qb + 8 * rr + 4 * g);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl_t + 32 * qb + 8 * rr + 4 * g);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rr + e;
+        const float raw = cx.sgn * s[qb][r];
+        float x, th = 0.0f;
+        if (kSoftcap) {
+          const float ex = fast_exp2(raw * cx.cap_k2);
+          th = 1.0f - 2.0f * fast_rcp(ex + 1.0f);
+          x = cx.cap_log2 * th;
+        } else {
+          x = raw * cx.scale_log2;
+        }
+        if (kAlibi) {
+          const int i = q0 + roff(qb, r) + 4 * g;
+          x = __builtin_fmaf(-cx.slope_log2, fabsf(static_cast<float>(i + cx.delta_pos - my_key)), x);
+        }
+        const float p = fast_exp2(x - lv[e]);
+        float dsv = p * (dp[qb][r] - dlv[e]);
+        if (kSoftcap) dsv *= 1.0f - th * th;
+        s[qb][r] = p;
+        dp[qb][r] = dsv;
+      }
+    }
+  if (masked) {
+    const uint32_t span = static_cast<uint32_t>(rows_count);
+    const int ib = q0 + 4 * g - rows_first;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = static_cast<uint32_t>(ib + roff(qb, r)) < span;
+        s[qb][r] = ok ? s[qb][r] : 0.0f;
+        dp[qb][r] = ok ? dp[qb][r] : 0.0f;
+      }
+  }
+  bf16x8 pf[2][2], sf[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pf[qb][r >> 3][r & 7] = static_cast<__bf16>(s[qb][r]);
+      sf[qb][r >> 3][r & 7] = static_cast<__bf16>(dp[qb][r]);
+    }
+
+  // dV += P^T dO ; dK += dS^T Q  (the D/32 output blocks are independent)
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 fo[C::DBLK], fq[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) {
+      fo[db] = tr_frag<D>(dot_lds, kk, db, lane);
+      fq[db] = tr_frag<D>(qt_lds, kk, db, lane);
+    }
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) {
+      dv[db] = mfma32(pf[kk >> 1][kk & 1], fo[db], dv[db]);
+      dk[db] = mfma32(sf[kk >> 1][kk & 1], fq[db], dk[db]);
+    }
+  }
+}
+
+template <int D, int MOD>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial) {
+  using C = KVCfg<D>;
+  // Distinct LDS objects per buffer (see the forward kernel): the copy of the
+  // next Q / dO tile then overlaps the work on the current one.
+  __shared__ __attribute__((aligned(16))) char lq0[C::TB];
+  __shared__ __attribute__((aligned(16))) char lq1[C::TB];
+  __shared__ __attribute__((aligned(16))) char ld0[C::TB];
+  __shared__ __attribute__((aligned(16))) char ld1[C::TB];
+  __shared__ __attribute__((aligned(16))) float ll0[C::BM];
+  __shared__ __attribute__((aligned(16))) float ll1[C::BM];
+  __shared__ __attribute__((aligned(16))) float lg0[C::BM];
+  __shared__ __attribute__((aligned(16))) float lg1[C::BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
   const int per = a.Hq * a.B;
   const int kt = blockIdx.x / per;  // key tiles near the start see the most causal rows
   const int rem = blockIdx.x % per;
@@ -131,7 +251,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   if ((a.Hq & 7) == 0) h = (h & 7) * (a.Hq >> 3) + (h >> 3);
   const int G = a.Hq / a.Hkv;
   const int kvh = h / G;
-  (void)nkt;
 
   const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
   const bf16_t* dop = static_cast<const bf16_t*>(a.dout) + b * a.do_sb + h * a.do_sh;
@@ -157,67 +276,49 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     vf[ds] = __builtin_bit_cast(bf16x8, vr);
   }
 
-  const float scale = a.scale;
-  const float scale_abs = fabsf(scale);
-  // A negative scale is applied by negating the raw dot product in the
-  // exponent (and the gradient's scale keeps its sign).
-  const float sgn = scale < 0.0f ? -1.0f : 1.0f;
-  const float scale_log2 = scale_abs * kLog2e;
-  const float cap_k2 = kSoftcap ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
-  const float cap_log2 = a.softcap * kLog2e;
-  const float slope_log2 = kAlibi ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
-  const int delta_pos = a.Sk - a.Sq;
+  const float scale_abs = fabsf(a.scale);
+  BwdCtx cx;
+  cx.scale_log2 = scale_abs * kLog2e;
+  cx.sgn = a.scale < 0.0f ? -1.0f : 1.0f;
+  cx.slope_log2 = (MOD & 1) ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
+  cx.cap_k2 = (MOD & 2) ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
+  cx.cap_log2 = a.softcap * kLog2e;
+  cx.delta_pos = a.Sk - a.Sq;
 
-  // Query tiles that meet this key tile: rows i with lo(i) <= last key and
-  // hi(i) >= first key of the workgroup's 128 keys.
+  // Query tiles that meet the workgroup's keys: rows i with lo(i) <= last key
+  // and hi(i) >= first key.
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
   const int c0 = kt * C::BN, c1 = min(a.Sk, c0 + C::BN) - 1;
   int i_lo = 0, i_hi = a.Sq - 1;
-  if (win.R != kUnbounded) i_lo = max(i_lo, c0 - delta_pos - win.R);
-  if (win.L != kUnbounded) i_hi = min(i_hi, c1 - delta_pos + win.L);
+  if (win.R != kUnbounded) i_lo = max(i_lo, c0 - cx.delta_pos - win.R);
+  if (win.L != kUnbounded) i_hi = min(i_hi, c1 - cx.delta_pos + win.L);
   const int qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
-  const int qt_end = i_lo <= i_hi ? i_hi / C::BM + 1 : 0;
-  const int ntiles = qt_end - qt_begin;
+  const int ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
+  int rows_first, rows_count;
+  win.key_rows(my_key, &rows_first, &rows_count);
 
-  uint4 qr[C::CPT], dr[C::CPT];
-  float lse_r = 0.0f;
-  auto load_regs = [&](int qt) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int row = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      const int i = qt * C::BM + row;
-      if (i < a.Sq) {
-        qr[u] = *reinterpret_cast<const uint4*>(qp + (int64_t)i * a.q_ss + col);
-        dr[u] = *reinterpret_cast<const uint4*>(dop + (int64_t)i * a.do_ss + col);
-      } else {
-        qr[u] = make_uint4(0, 0, 0, 0);
-        dr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  float small_r = 0.0f;  // lse2 (threads 0..63) or Delta (threads 64..127) of the next tile
+  auto load_tile = [&](int qt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lq1 : lq0), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? ld1 : ld0), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
     if (tid < 2 * C::BM) {
       const int i = qt * C::BM + (tid & (C::BM - 1));
       if (tid < C::BM) {
         const float l = i < a.Sq ? lsep[i] : kNegInf;
-        lse_r = l == kNegInf ? kPosInf : l * kLog2e;  // empty rows: P = 0
+        small_r = l == kNegInf ? kPosInf : l * kLog2e;  // empty or padding rows: P = 0
       } else {
-        lse_r = i < a.Sq ? dlp[i] : 0.0f;
+        small_r = i < a.Sq ? dlp[i] : 0.0f;
       }
     }
   };
-  auto store_regs = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int row = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(lds_q + buf * C::QT + row * C::QS + col) = qr[u];
-      *reinterpret_cast<uint4*>(lds_do + buf * C::QT + row * C::QS + col) = dr[u];
-    }
-    if (tid < C::BM) lds_lse[buf * C::BM + tid] = lse_r;
-    else if (tid < 2 * C::BM) lds_dl[buf * C::BM + tid - C::BM] = lse_r;
+  auto store_small = [&](auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (tid < C::BM) (BUF ? ll1 : ll0)[tid] = small_r;
+    else if (tid < 2 * C::BM) (BUF ? lg1 : lg0)[tid - C::BM] = small_r;
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   f32x16 dv[C::DBLK], dk[C::DBLK];
 #pragma unroll
@@ -229,89 +330,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     }
 
   if (ntiles > 0) {
-    load_regs(qt_begin);
-    store_regs(0);
+    load_tile(qt_begin, B0{});
+    store_small(B0{});
   }
+  wait_dma();
   __syncthreads();
 
-  const int beta = lane >> 4, s16 = lane & 15;
-  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
-  const int tr_col = 16 * (beta & 1) + 4 * (s16 & 3);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  const int kw = kv0 / 32;  // this wave's 32-key block index
+  auto step = [&](int t, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using NEXT = std::integral_constant<int, 1 - BUF>;
     const int qt = qt_begin + t;
     const bool has_next = t + 1 < ntiles;
-    if (has_next) load_regs(qt + 1);
-
-    // Is this (32-query x 32-key) block wholly allowed?  Same interval test
-    // as the forward's tile classification, for this wave's 32 keys.
-    const TileRange tr_q(win, qt, C::BM, 32);
-    const int kt32 = kv0 / 32;
-    const bool full = tr_q.full(kt32);
-    const bool any = kt32 >= tr_q.kt_begin && kt32 < tr_q.kt_end;
-
-    if (any) {
-      const bf16_t* qb = lds_q + buf * C::QT;
-      const bf16_t* dob = lds_do + buf * C::QT;
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.0f;
-        dp[r] = 0.0f;
-      }
-#pragma unroll
-      for (int ds = 0; ds < C::DSTEPS; ++ds) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + c * C::QS + 16 * ds + 8 * g);
-        s = mfma32(qa, kf[ds], s);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(dob + c * C::QS + 16 * ds + 8 * g);
-        dp = mfma32(da, vf[ds], dp);
-      }
-      // s[r]: query q0 + 8*(r/4) + 4*g + r%4, key my_key.
-      const float* lse_t = lds_lse + buf * C::BM;
-      const float* dl_t = lds_dl + buf * C::BM;
-      const int q0 = qt * C::BM;
-      bf16x8 pf[2], sf[2];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 8 * rr + 4 * g);
-        const float4 d4 = *reinterpret_cast<const float4*>(dl_t + 8 * rr + 4 * g);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rr + e;
-          const int i = q0 + 8 * rr + 4 * g + e;
-          float th = 0.0f;
-          const float x = score_x<kAlibi, kSoftcap>(sgn * s[r], scale_log2, cap_k2, cap_log2,
-                                                    slope_log2, i + delta_pos - my_key, &th);
-          float p = fast_exp2(x - lv[e]);
-          if (!full && !mask_ok(a.mask, a.Sq, a.Sk, i, my_key)) p = 0.0f;
-          float dsv = p * (dp[r] - dvv[e]);
-          if (kSoftcap) dsv *= 1.0f - th * th;
-          pf[r >> 3][r & 7] = static_cast<__bf16>(p);
-          sf[r >> 3][r & 7] = static_cast<__bf16>(dsv);
-        }
-      }
-      // dV += P^T dO ; dK += dS^T Q   (B operands: transposed tile reads)
-#pragma unroll
-      for (int db = 0; db < C::DBLK; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int off = (16 * ks + tr_row) * C::QS + 32 * db + tr_col;
-          const bf16x8 dob_f = cat_frag(lds_read_tr16(dob + off), lds_read_tr16(dob + off + 8 * C::QS));
-          dv[db] = mfma32(pf[ks], dob_f, dv[db]);
-          const bf16x8 qb_f = cat_frag(lds_read_tr16(qb + off), lds_read_tr16(qb + off + 8 * C::QS));
-          dk[db] = mfma32(sf[ks], qb_f, dk[db]);
-        }
-      }
-    }
-
-    if (has_next) store_regs(buf ^ 1);
+    if (has_next) load_tile(qt + 1, NEXT{});
+    const TileRange trq(win, qt, C::BM, 32);
+    if (kw >= trq.kt_begin && kw < trq.kt_end)
+      dkdv_tile<D, MOD>(BUF ? lq1 : lq0, BUF ? ld1 : ld0, BUF ? ll1 : ll0, BUF ? lg1 : lg0, kf, vf,
+                        dk, dv, cx, qt * C::BM, my_key, !trq.full(kw), rows_first, rows_count,
+                        lane);
+    if (has_next) store_small(NEXT{});
+    wait_dma();
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B0{});
+    step(t + 1, B1{});
   }
+  if (t < ntiles) step(t, B0{});
 
   // dv[db][r], dk[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c.
+  const float scale = a.scale;
 #pragma unroll
   for (int db = 0; db < C::DBLK; ++db) {
 #pragma unroll
@@ -367,25 +416,91 @@ template <int D>
 struct QCfg {
   static constexpr int BM = 128;           // query rows per workgroup (4 waves x 32)
   static constexpr int BN = 64;            // keys per streamed tile
-  static constexpr int NT = 256;
-  static constexpr int KS = D + 8;         // K tile stride (row reads and transposed reads)
-  static constexpr int VS = D + 8;         // V tile stride (row reads)
-  static constexpr int KT = BN * KS;
-  static constexpr int VT = BN * VS;
-  static constexpr int CPT = BN * D / 8 / NT;
+  using L = TileLayout<D>;
+  static constexpr int TB = L::BYTES;
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
 };
 
-template <int D, int MOD>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
+// One 64-key tile: S^T = K Q^T and dP^T = V dO^T (one query per lane),
+// dS^T from the saved LSE and Delta, dQ^T += K^T dS^T.
+template <int D, int MOD, bool MASKED>
+__device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, const bf16x8 (&qf)[D / 16],
+                                        const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32],
+                                        const BwdCtx& cx, float lse2, float dl, int my_q, int key_base,
+                                        int row_first, int row_count, int lane) {
   using C = QCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * C::KT];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * C::VT];
+  const int g = lane >> 5, c = lane & 31;
+  f32x16 s[2], dp[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[kb][r] = 0.0f;
+      dp[kb][r] = 0.0f;
+    }
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    bf16x8 ka[2], va[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      ka[kb] = row_frag<D>(kt_lds, 32 * kb + c, ds, g);
+      va[kb] = row_frag<D>(vt_lds, 32 * kb + c, ds, g);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = mfma32(ka[kb], qf[ds], s[kb]);
+      dp[kb] = mfma32(va[kb], df[ds], dp[kb]);
+    }
+  }
+  const uint32_t span = static_cast<uint32_t>(row_count);
+  const int jb = key_base + 4 * g - row_first;
+  bf16x8 sf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float raw = cx.sgn * s[kb][r];
+      float x, th = 0.0f;
+      if (kSoftcap) {
+        const float ex = fast_exp2(raw * cx.cap_k2);
+        th = 1.0f - 2.0f * fast_rcp(ex + 1.0f);
+        x = cx.cap_log2 * th;
+      } else {
+        x = raw * cx.scale_log2;
+      }
+      if (kAlibi) {
+        const int j = key_base + 4 * g + roff(kb, r);
+        x = __builtin_fmaf(-cx.slope_log2, fabsf(static_cast<float>(my_q + cx.delta_pos - j)), x);
+      }
+      float p = fast_exp2(x - lse2);
+      if (MASKED) p = static_cast<uint32_t>(jb + roff(kb, r)) < span ? p : 0.0f;
+      float dsv = p * (dp[kb][r] - dl);
+      if (kSoftcap) dsv *= 1.0f - th * th;
+      sf[kb][r >> 3][r & 7] = static_cast<__bf16>(dsv);
+    }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 ka[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) ka[db] = tr_frag<D>(kt_lds, kk, db, lane);
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) dq[db] = mfma32(ka[db], sf[kk >> 1][kk & 1], dq[db]);
+  }
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int D, int MOD>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using C = QCfg<D>;
+  __shared__ __attribute__((aligned(16))) char lk0[C::TB];
+  __shared__ __attribute__((aligned(16))) char lk1[C::TB];
+  __shared__ __attribute__((aligned(16))) char lv0[C::TB];
+  __shared__ __attribute__((aligned(16))) char lv1[C::TB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
   const int nqt = (a.Sq + C::BM - 1) / C::BM;
   const int per = a.Hq * a.B;
@@ -415,14 +530,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
     qf[ds] = __builtin_bit_cast(bf16x8, r1);
     df[ds] = __builtin_bit_cast(bf16x8, r2);
   }
-  const float scale = a.scale;
-  const float scale_abs = fabsf(scale);
-  const float sgn = scale < 0.0f ? -1.0f : 1.0f;
-  const float scale_log2 = scale_abs * kLog2e;
-  const float cap_k2 = kSoftcap ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
-  const float cap_log2 = a.softcap * kLog2e;
-  const float slope_log2 = kAlibi ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
-  const int delta_pos = a.Sk - a.Sq;
+  const float scale_abs = fabsf(a.scale);
+  BwdCtx cx;
+  cx.scale_log2 = scale_abs * kLog2e;
+  cx.sgn = a.scale < 0.0f ? -1.0f : 1.0f;
+  cx.slope_log2 = (MOD & 1) ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
+  cx.cap_k2 = (MOD & 2) ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
+  cx.cap_log2 = a.softcap * kLog2e;
+  cx.delta_pos = a.Sk - a.Sq;
   float lse2 = kPosInf, dl = 0.0f;
   if (q_ok) {
     const float l = a.lse[((int64_t)b * a.Hq + h) * a.Sq + my_q];
@@ -433,34 +548,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
   const TileRange range(win, qt, C::BM, C::BN);
   const int ntiles = range.kt_end - range.kt_begin;
+  const int nfull = range.n_full();
+  int row_first, row_count;
+  win.row_keys(my_q, &row_first, &row_count);
 
-  uint4 kr[C::CPT], vr[C::CPT];
-  auto load_regs = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int row = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      const int key = kt * C::BN + row;
-      if (key < a.Sk) {
-        kr[u] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * a.k_ss + col);
-        vr[u] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * a.v_ss + col);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  auto load_tile = [&](int kt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lk1 : lk0), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lv1 : lv0), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
   };
-  auto store_regs = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int row = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(lds_k + buf * C::KT + row * C::KS + col) = kr[u];
-      *reinterpret_cast<uint4*>(lds_v + buf * C::VT + row * C::VS + col) = vr[u];
-    }
-  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   f32x16 dq[C::DBLK];
 #pragma unroll
@@ -468,79 +566,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
 
-  if (ntiles > 0) {
-    load_regs(range.kt_begin);
-    store_regs(0);
-  }
+  if (ntiles > 0) load_tile(range.kt_at(0), B0{});
+  wait_dma();
   __syncthreads();
 
-  const int beta = lane >> 4, s16 = lane & 15;
-  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
-  const int tr_col = 16 * (beta & 1) + 4 * (s16 & 3);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kt = range.kt_begin + t;
-    const bool full = range.full(kt);
+  auto step = [&](int t, auto buf_tag, auto masked) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using NEXT = std::integral_constant<int, 1 - BUF>;
+    const int kt = range.kt_at(t);
     const bool has_next = t + 1 < ntiles;
-    if (has_next) load_regs(kt + 1);
-
-    const bf16_t* kb = lds_k + buf * C::KT;
-    const bf16_t* vb = lds_v + buf * C::VT;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[h2][r] = 0.0f;
-        dp[h2][r] = 0.0f;
-      }
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + (32 * h2 + c) * C::KS + 16 * ds + 8 * g);
-        s[h2] = mfma32(ka, qf[ds], s[h2]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + (32 * h2 + c) * C::VS + 16 * ds + 8 * g);
-        dp[h2] = mfma32(va, df[ds], dp[h2]);
-      }
-    }
-    // s[h2][r]: key kt*BN + 32*h2 + 8*(r/4) + 4*g + r%4, query my_q.
-    bf16x8 sf[2][2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kt * C::BN + 32 * h2 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float th = 0.0f;
-        const float x = score_x<kAlibi, kSoftcap>(sgn * s[h2][r], scale_log2, cap_k2, cap_log2,
-                                                  slope_log2, my_q + delta_pos - j, &th);
-        float p = fast_exp2(x - lse2);
-        if (!full && !mask_ok(a.mask, a.Sq, a.Sk, my_q, j)) p = 0.0f;
-        float dsv = p * (dp[h2][r] - dl);
-        if (kSoftcap) dsv *= 1.0f - th * th;
-        sf[h2][r >> 3][r & 7] = static_cast<__bf16>(dsv);
-      }
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16_t* p0 = kb + (32 * h2 + 16 * ks + tr_row) * C::KS + 32 * db + tr_col;
-          const bf16x8 ka = cat_frag(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * C::KS));
-          dq[db] = mfma32(ka, sf[h2][ks], dq[db]);
-        }
-      }
-    }
-
-    if (has_next) store_regs(buf ^ 1);
+    if (has_next) load_tile(range.kt_at(t + 1), NEXT{});
+    dq_tile<D, MOD, decltype(masked)::value>(BUF ? lk1 : lk0, BUF ? lv1 : lv0, qf, df, dq, cx, lse2, dl,
+                                             my_q, kt * C::BN, row_first, row_count, lane);
+    wait_dma();
     __syncthreads();
+  };
+  using FULL = std::false_type;
+  using PART = std::true_type;
+  int t = 0;
+  for (; t + 1 < nfull; t += 2) {
+    step(t, B0{}, FULL{});
+    step(t + 1, B1{}, FULL{});
   }
+  if (t < nfull) step(t++, B0{}, FULL{});
+  if (t < ntiles && (t & 1)) step(t++, B1{}, PART{});
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, B0{}, PART{});
+    step(t + 1, B1{}, PART{});
+  }
+  if (t < ntiles) step(t++, B0{}, PART{});
 
   if (q_ok) {
+    const float scale = a.scale;
     bf16_t* out = static_cast<bf16_t*>(a.dq) + b * a.dq_sb + (int64_t)my_q * a.dq_ss + h * a.dq_sh;
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) {

@@ -134,6 +134,26 @@ struct RowWindow {
     int v = i + delta + R;
     return v > Sk - 1 ? Sk - 1 : v;
   }
+  // Allowed keys of row i as [*first, *first + *count) (count 0: none).
+  __host__ __device__ void row_keys(int i, int* first, int* count) const {
+    *first = 0;
+    *count = 0;
+    if (i < 0 || i >= Sq || !row_nonempty(i)) return;
+    *first = lo(i);
+    *count = hi(i) - *first + 1;
+  }
+  // Rows that may attend key j as [*first, *first + *count): the rows i with
+  // i + delta - L <= j <= i + delta + R, clipped to [0, Sq).
+  __host__ __device__ void key_rows(int j, int* first, int* count) const {
+    *first = 0;
+    *count = 0;
+    if (j < 0 || j >= Sk) return;
+    const int a = R == kUnbounded ? 0 : max(0, j - delta - R);
+    const int b = L == kUnbounded ? Sq - 1 : min(Sq - 1, j - delta + L);
+    if (b < a) return;
+    *first = a;
+    *count = b - a + 1;
+  }
 };
 
 // Tiles of one row block [r0, r0 + bm) against key tiles of width bn.
