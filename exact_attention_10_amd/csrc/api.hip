@@ -274,7 +274,9 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
   a.mask = mask_from(p);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   a.delta = static_cast<float*>(workspace);
-  char* rest = static_cast<char*>(workspace) + up((size_t)p->B * p->Hq * p->Sq * sizeof(float));
+  const size_t rows_bytes = up((size_t)p->B * p->Hq * p->Sq * sizeof(float));
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + rows_bytes);
+  char* rest = static_cast<char*>(workspace) + 2 * rows_bytes;
   const size_t part = up((size_t)p->B * p->Sk * p->Hq * p->D * sizeof(float));
   a.part_dk = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest) : nullptr;
   a.part_dv = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest + part) : nullptr;

@@ -40,7 +40,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPosInf = __builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
-// 1. Delta = rowsum(dO * O), one 16-lane group per (b, i, h) row.
+// 1. Delta = rowsum(dO * O), one 16-lane group per (b, i, h) row; the same
+//    pass stores the LSE in exp2 units for the dK/dV kernel.
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -68,17 +69,48 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) a.delta[((int64_t)b * a.Hq + h) * a.Sq + i] = acc;
+  if (row < rows && part == 0) {
+    const int64_t idx = ((int64_t)b * a.Hq + h) * a.Sq + i;
+    a.delta[idx] = acc;
+    const float l = a.lse[idx];
+    a.lse2[idx] = l == kNegInf ? kPosInf : l * kLog2e;  // empty rows: P = 0
+  }
 }
 
 struct BwdCtx {
-  float scale_log2;   // |scale| * log2(e)
-  float sgn;          // sign of the scale (applied to the raw dot product)
+  float scale_log2;   // scale * log2(e) (signed)
   float slope_log2;   // ALiBi slope * log2(e)
-  float cap_k2;       // 2 log2(e) |scale| / softcap
+  float cap_k2;       // 2 log2(e) scale / softcap (signed)
   float cap_log2;     // softcap * log2(e)
   int delta_pos;      // Sk - Sq
 };
+
+__device__ __forceinline__ BwdCtx make_ctx(const BwdArgs& a, int b, int h, bool alibi, bool softcap) {
+  BwdCtx cx;
+  cx.scale_log2 = a.scale * kLog2e;
+  cx.slope_log2 = alibi ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
+  cx.cap_k2 = softcap ? 2.0f * kLog2e * a.scale / a.softcap : 0.0f;
+  cx.cap_log2 = a.softcap * kLog2e;
+  cx.delta_pos = a.Sk - a.Sq;
+  return cx;
+}
+
+// exp2-domain score minus the row's lse2 for raw dot product s; *th gets
+// tanh of the capped score (softcap only).  dist = query position - key.
+template <bool kAlibi, bool kSoftcap>
+__device__ __forceinline__ float score_minus(float s, float lse2, const BwdCtx& cx, int dist, float* th) {
+  if (!kAlibi && !kSoftcap) return __builtin_fmaf(s, cx.scale_log2, -lse2);
+  float x;
+  if (kSoftcap) {
+    const float ex = fast_exp2(s * cx.cap_k2);
+    *th = 1.0f - 2.0f * fast_rcp(ex + 1.0f);
+    x = cx.cap_log2 * *th;
+  } else {
+    x = s * cx.scale_log2;
+  }
+  if (kAlibi) x = __builtin_fmaf(-cx.slope_log2, fabsf(static_cast<float>(dist)), x);
+  return x - lse2;
+}
 
 // Key offset (within a 64-row tile, relative to 4*g) of accumulator
 // register r of 32-row block kb: rows 8*(r/4) + r%4 of a 32x32 MFMA result.
@@ -168,20 +200,9 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rr + e;
-        const float raw = cx.sgn * s[qb][r];
-        float x, th = 0.0f;
-        if (kSoftcap) {
-          const float ex = fast_exp2(raw * cx.cap_k2);
-          th = 1.0f - 2.0f * fast_rcp(ex + 1.0f);
-          x = cx.cap_log2 * th;
-        } else {
-          x = raw * cx.scale_log2;
-        }
-        if (kAlibi) {
-          const int i = q0 + roff(qb, r) + 4 * g;
-          x = __builtin_fmaf(-cx.slope_log2, fabsf(static_cast<float>(i + cx.delta_pos - my_key)), x);
-        }
-        const float p = fast_exp2(x - lv[e]);
+        float th = 0.0f;
+        const int i = q0 + roff(qb, r) + 4 * g;
+        const float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[qb][r], lv[e], cx, i + cx.delta_pos - my_key, &th));
         float dsv = p * (dp[qb][r] - dlv[e]);
         if (kSoftcap) dsv *= 1.0f - th * th;
         s[qb][r] = p;
@@ -229,16 +250,22 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
 template <int D, int MOD>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial) {
   using C = KVCfg<D>;
-  // Distinct LDS objects per buffer (see the forward kernel): the copy of the
-  // next Q / dO tile then overlaps the work on the current one.
+  // Three buffers (one workgroup per CU leaves the LDS room): the copies of
+  // tiles t+1 and t+2 are in flight while tile t is processed.  Distinct LDS
+  // objects per buffer let alias analysis see that a copy never targets the
+  // buffer being read, so no wait for it is placed before the reads.
   __shared__ __attribute__((aligned(16))) char lq0[C::TB];
   __shared__ __attribute__((aligned(16))) char lq1[C::TB];
+  __shared__ __attribute__((aligned(16))) char lq2[C::TB];
   __shared__ __attribute__((aligned(16))) char ld0[C::TB];
   __shared__ __attribute__((aligned(16))) char ld1[C::TB];
+  __shared__ __attribute__((aligned(16))) char ld2[C::TB];
   __shared__ __attribute__((aligned(16))) float ll0[C::BM];
   __shared__ __attribute__((aligned(16))) float ll1[C::BM];
+  __shared__ __attribute__((aligned(16))) float ll2[C::BM];
   __shared__ __attribute__((aligned(16))) float lg0[C::BM];
   __shared__ __attribute__((aligned(16))) float lg1[C::BM];
+  __shared__ __attribute__((aligned(16))) float lg2[C::BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   const bf16_t* dop = static_cast<const bf16_t*>(a.dout) + b * a.do_sb + h * a.do_sh;
   const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.k_sb + kvh * a.k_sh;
   const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.v_sb + kvh * a.v_sh;
-  const float* lsep = a.lse + ((int64_t)b * a.Hq + h) * a.Sq;
+  const float* lsep = a.lse2 + ((int64_t)b * a.Hq + h) * a.Sq;
   const float* dlp = a.delta + ((int64_t)b * a.Hq + h) * a.Sq;
 
   const int kv0 = kt * C::BN + wave * 32;  // this wave's first key
@@ -275,15 +302,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     kf[ds] = __builtin_bit_cast(bf16x8, kr);
     vf[ds] = __builtin_bit_cast(bf16x8, vr);
   }
-
-  const float scale_abs = fabsf(a.scale);
-  BwdCtx cx;
-  cx.scale_log2 = scale_abs * kLog2e;
-  cx.sgn = a.scale < 0.0f ? -1.0f : 1.0f;
-  cx.slope_log2 = (MOD & 1) ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
-  cx.cap_k2 = (MOD & 2) ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
-  cx.cap_log2 = a.softcap * kLog2e;
-  cx.delta_pos = a.Sk - a.Sq;
+  const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
 
   // Query tiles that meet the workgroup's keys: rows i with lo(i) <= last key
   // and hi(i) >= first key.
@@ -297,28 +316,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   int rows_first, rows_count;
   win.key_rows(my_key, &rows_first, &rows_count);
 
-  float small_r = 0.0f;  // lse2 (threads 0..63) or Delta (threads 64..127) of the next tile
+  // Every wave issues the same number of memory operations per tile (its
+  // share of the Q and dO rows, plus one 64-float row: lse2 for even waves,
+  // Delta for odd ones -- waves 2 and 3 repeat waves 0 and 1), so one
+  // counter value means "all but the newest tile have landed".
+  constexpr int kOpsPerTile = 2 * (64 / C::L::RG / 4) + 1;
   auto load_tile = [&](int qt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
-    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lq1 : lq0), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
-    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? ld1 : ld0), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
-    if (tid < 2 * C::BM) {
-      const int i = qt * C::BM + (tid & (C::BM - 1));
-      if (tid < C::BM) {
-        const float l = i < a.Sq ? lsep[i] : kNegInf;
-        small_r = l == kNegInf ? kPosInf : l * kLog2e;  // empty or padding rows: P = 0
-      } else {
-        small_r = i < a.Sq ? dlp[i] : 0.0f;
-      }
+    char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
+    char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
+    float* ld = (wave & 1) ? (BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2))
+                           : (BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2));
+    tile_dma<D>(reinterpret_cast<bf16_t*>(qd), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(dd), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
+    // rows past Sq repeat the last row; they are masked on partial tiles
+    const int i = min(qt * C::BM + lane, a.Sq - 1);
+    __builtin_amdgcn_global_load_lds((wave & 1) ? dlp + i : lsep + i,
+                                     (__attribute__((address_space(3))) void*)ld, 4, 0, 0);
+  };
+  auto wait_older = [&](bool newest_in_flight) {
+    if (newest_in_flight) {
+      if constexpr (kOpsPerTile == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    } else {
+      wait_dma();
     }
   };
-  auto store_small = [&](auto buf_tag) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    if (tid < C::BM) (BUF ? ll1 : ll0)[tid] = small_r;
-    else if (tid < 2 * C::BM) (BUF ? lg1 : lg0)[tid - C::BM] = small_r;
-  };
+  static_assert(kOpsPerTile == 9 || kOpsPerTile == 5, "ops per tile");
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
 
   f32x16 dv[C::DBLK], dk[C::DBLK];
 #pragma unroll
@@ -329,35 +356,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       dk[db][r] = 0.0f;
     }
 
-  if (ntiles > 0) {
-    load_tile(qt_begin, B0{});
-    store_small(B0{});
-  }
-  wait_dma();
+  if (ntiles > 0) load_tile(qt_begin, B0{});
+  if (ntiles > 1) load_tile(qt_begin + 1, B1{});
+  wait_older(ntiles > 1);
   __syncthreads();
 
   const int kw = kv0 / 32;  // this wave's 32-key block index
   auto step = [&](int t, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
-    using NEXT = std::integral_constant<int, 1 - BUF>;
+    using AHEAD = std::integral_constant<int, (BUF + 2) % 3>;
     const int qt = qt_begin + t;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(qt + 1, NEXT{});
+    const bool ahead = t + 2 < ntiles;
+    if (ahead) load_tile(qt + 2, AHEAD{});
     const TileRange trq(win, qt, C::BM, 32);
     if (kw >= trq.kt_begin && kw < trq.kt_end)
-      dkdv_tile<D, MOD>(BUF ? lq1 : lq0, BUF ? ld1 : ld0, BUF ? ll1 : ll0, BUF ? lg1 : lg0, kf, vf,
-                        dk, dv, cx, qt * C::BM, my_key, !trq.full(kw), rows_first, rows_count,
+      dkdv_tile<D, MOD>(BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2), BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2),
+                        BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2), BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2),
+                        kf, vf, dk, dv, cx, qt * C::BM, my_key, !trq.full(kw), rows_first, rows_count,
                         lane);
-    if (has_next) store_small(NEXT{});
-    wait_dma();
+    wait_older(ahead);  // tile t + 1 has landed
     __syncthreads();
   };
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  for (; t + 2 < ntiles; t += 3) {
     step(t, B0{});
     step(t + 1, B1{});
+    step(t + 2, B2{});
   }
-  if (t < ntiles) step(t, B0{});
+  if (t < ntiles) step(t++, B0{});
+  if (t < ntiles) step(t++, B1{});
 
   // dv[db][r], dk[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c.
   const float scale = a.scale;
@@ -462,20 +489,9 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float raw = cx.sgn * s[kb][r];
-      float x, th = 0.0f;
-      if (kSoftcap) {
-        const float ex = fast_exp2(raw * cx.cap_k2);
-        th = 1.0f - 2.0f * fast_rcp(ex + 1.0f);
-        x = cx.cap_log2 * th;
-      } else {
-        x = raw * cx.scale_log2;
-      }
-      if (kAlibi) {
-        const int j = key_base + 4 * g + roff(kb, r);
-        x = __builtin_fmaf(-cx.slope_log2, fabsf(static_cast<float>(my_q + cx.delta_pos - j)), x);
-      }
-      float p = fast_exp2(x - lse2);
+      float th = 0.0f;
+      const int j = key_base + 4 * g + roff(kb, r);
+      float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[kb][r], lse2, cx, my_q + cx.delta_pos - j, &th));
       if (MASKED) p = static_cast<uint32_t>(jb + roff(kb, r)) < span ? p : 0.0f;
       float dsv = p * (dp[kb][r] - dl);
       if (kSoftcap) dsv *= 1.0f - th * th;
@@ -530,14 +546,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     qf[ds] = __builtin_bit_cast(bf16x8, r1);
     df[ds] = __builtin_bit_cast(bf16x8, r2);
   }
-  const float scale_abs = fabsf(a.scale);
-  BwdCtx cx;
-  cx.scale_log2 = scale_abs * kLog2e;
-  cx.sgn = a.scale < 0.0f ? -1.0f : 1.0f;
-  cx.slope_log2 = (MOD & 1) ? a.alibi[b * a.alibi_sb + h] * kLog2e : 0.0f;
-  cx.cap_k2 = (MOD & 2) ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
-  cx.cap_log2 = a.softcap * kLog2e;
-  cx.delta_pos = a.Sk - a.Sq;
+  const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
   float lse2 = kPosInf, dl = 0.0f;
   if (q_ok) {
     const float l = a.lse[((int64_t)b * a.Hq + h) * a.Sq + my_q];
@@ -657,7 +666,7 @@ hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
 
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  size_t n = up((size_t)B * Hq * Sq * sizeof(float));
+  size_t n = 2 * up((size_t)B * Hq * Sq * sizeof(float));  // Delta, lse2
   if (Hkv > 0 && Hq / Hkv > 1) n += 2 * up((size_t)B * Sk * Hq * D * sizeof(float));
   return n;
 }

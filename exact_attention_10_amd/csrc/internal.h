@@ -74,6 +74,7 @@ struct BwdArgs {
   float softcap;
   MaskArgs mask;
   float* delta;              // workspace [B, Hq, Sq]
+  float* lse2;               // workspace [B, Hq, Sq]: lse * log2(e), +inf for empty rows
   float* part_dk;            // workspace [B, Sk, Hq, D] (grouped heads only)
   float* part_dv;
 };
