@@ -308,27 +308,11 @@ size_t attn_bwd_workspace_size(const attn_params* p) {
   return attn::bwd_workspace_bytes(p->B, p->Hq, p->Hkv, p->Sq, p->Sk, p->D);
 }
 
-// Keys per split for decode when the caller does not choose: enough splits
-// that B * splits covers the GPU several times, chunks a multiple of 64.
-static int decode_chunk(const attn_params* p, int32_t num_splits) {
-  const int smax = p->Sk > 0 ? p->Sk : 1;
-  int splits = num_splits;
-  if (splits <= 0) {
-    const int target_wg = 1024;
-    splits = (target_wg + p->B - 1) / (p->B > 0 ? p->B : 1);
-    if (splits < 1) splits = 1;
-  }
-  int chunk = (smax + splits - 1) / splits;
-  chunk = (chunk + 63) / 64 * 64;
-  if (chunk < 256 && num_splits <= 0) chunk = 256;
-  return chunk;
-}
-
 size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits) {
-  if (p == nullptr || p->B <= 0 || p->Hq <= 0 || p->D <= 0 || p->Sk <= 0) return 0;
-  const int chunk = decode_chunk(p, num_splits);
-  const int max_splits = (p->Sk + chunk - 1) / chunk;
-  return attn::decode_workspace_bytes(p->B, p->Hq, p->D, max_splits);
+  if (p == nullptr || p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 || p->Sk <= 0 ||
+      num_splits < 0 || num_splits > 65536)
+    return 0;
+  return attn::decode_workspace(p->B, p->Hq, p->Hkv, p->D, attn::decode_parts(num_splits)).bytes;
 }
 
 attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache,
@@ -351,7 +335,8 @@ attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache
   if ((st = check_tensor("o", o, dt, p->B, 1, p->Hq, true)) != ATTN_OK) return st;
   if (p->B > 0 && (cache_seqlens == nullptr || lse == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "cache_seqlens and lse must not be NULL");
-  if (num_splits < 0) return fail(ATTN_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (num_splits < 0 || num_splits > 65536)
+    return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [0, 65536] (got %d)", num_splits);
   if (p->B == 0) return ATTN_OK;
   const size_t need = attn_decode_workspace_size(p, num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
@@ -370,11 +355,13 @@ attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.D = p->D; a.Smax = p->Sk;
   a.scale = cm.scale;
   a.softcap = p->softcap;
-  a.chunk = decode_chunk(p, num_splits);
-  a.max_splits = p->Sk > 0 ? (p->Sk + a.chunk - 1) / a.chunk : 0;
-  const size_t opart = static_cast<size_t>(p->B) * a.max_splits * p->Hq * p->D * sizeof(float);
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((opart + 255) / 256) * 256);
+  a.parts = attn::decode_parts(num_splits);
+  a.nhg = attn::decode_head_groups(p->Hq, p->Hkv);
+  const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->D, a.parts);
+  char* wsb = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(wsb + wl.o_off);
+  a.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
+  a.job_seg = reinterpret_cast<int32_t*>(wsb + wl.seg_off);
   return hip_status(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
 }
 

@@ -63,6 +63,44 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Max without NaN canonicalisation.  Inline assembly gets no hazard wait
+// states from the compiler: never feed it a matrix-core result directly.
+__device__ __forceinline__ float max_nc(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nc(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Both halves' values of x in every lane, without an LDS round trip:
+// v_permlane32_swap exchanges lanes 32..63 of its first register with lanes
+// 0..31 of its second, so on two copies of x lane l ends with x[l % 32] in the
+// first and x[l % 32 + 32] in the second.  (Written as assembly on two
+// read-write operands, because the compiler builtin's second result was found
+// folded onto the first; the s_nops cover the VALU-write -> permlane-read and
+// permlane-write -> VALU-read hazards that the compiler does not see here.)
+__device__ __forceinline__ void halves32(float x, float* lo, float* hi) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  *lo = a;
+  *hi = b;
+}
+// Max / sum of x with the value in lane l ^ 32.
+__device__ __forceinline__ float pair_max32(float x) {
+  float lo, hi;
+  halves32(x, &lo, &hi);
+  return max_nc(lo, hi);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  float lo, hi;
+  halves32(x, &lo, &hi);
+  return lo + hi;
+}
+
 // LDS image of a 64-row x D bf16 tile written by direct global->LDS loads.
 // A global_load_lds_dwordx4 instruction stores 16 bytes per lane at
 // consecutive 16-byte slots of a wave-uniform LDS base, so one instruction
@@ -105,6 +143,26 @@ __device__ __forceinline__ void tile_dma(bf16_t* tile, const bf16_t* src, int64_
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One global_load_lds_dwordx4 issued from inline assembly: lane i's 16 bytes
+// at gptr land at LDS byte lds_base + 16 * i (lds_base wave-uniform, via M0).
+// The compiler does not count these copies, so it adds no waits for them
+// before LDS reads; the caller orders them with its own vmcnt waits.  All
+// later VMEM waits the compiler emits stay correct (they can only over-wait,
+// since the counter retires in order).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Per-row allowed key interval for causal / sliding-window masks.
 // With delta = Sk - Sq, row i may attend keys j with

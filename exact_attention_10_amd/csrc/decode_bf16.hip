@@ -2,19 +2,34 @@
 //
 // flash_attn_with_kvcache ("FlashAttention: Fast and Memory-Efficient Exact
 // Attention", "Examples") attends one new query per sequence to the first
-// cache_seqlens[b] rows of that sequence's cache.  Here each sequence's
-// valid prefix is cut into chunks of `chunk` keys; one workgroup attends all
-// query heads of one kv head to one chunk and writes a partial result
-// (normalised O_s in fp32 and its log-sum-exp), and a second kernel merges
-// the chunks of each sequence with the LSE-weighted combine
+// cache_seqlens[b] rows of that sequence's cache.  The key work is split and
+// merged with the LSE-weighted combine
 //   lse = log sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) O_s
 // (the chunk-level form of the online softmax of "Accelerating AI: A Deep
 // Dive into Flash Attention", "2. Online Softmax").
 //
-// With multi-query heads (128 query heads reading one kv head) the query
-// heads play the role of query rows: the matrix-core tiles are the same as in
-// the forward kernel, S^T = K Q^T with 32 heads per wave, so each K/V byte
-// read from HBM feeds 128 heads.
+// Work decomposition.  A job is one (sequence b, kv head, group of up to 128
+// query heads of that kv head); its keys are cut into 32-key steps.  All
+// jobs' steps, in job order, form one list of S steps that is cut into
+// Pe = min(P, S) equal contiguous ranges, one per workgroup (P = one per
+// compute unit by default), so every workgroup streams the same number of K/V
+// bytes whatever the mix of cache lengths.  A range that spans several jobs
+// produces one partial result per job; the partial of job j from workgroup w
+// goes to slot w + j (unique, since ranges are ordered).  The workgroups that
+// start and end a job record their index for the combine kernel.
+//
+// Inside a workgroup, 8 consumer waves: head block hb = wave % 4 (32 query
+// heads, so each K/V byte read from HBM serves all 128 heads of the job) and
+// step parity wave / 4 (the two waves of a head block share a SIMD, take
+// alternate 32-key steps and merge their running softmax states through LDS
+// at the end of the job's segment).  The query heads play the role of query
+// rows of the forward kernel: S^T = K Q^T on the 32x32x16 matrix core.  K/V
+// tiles stream through an NS-deep LDS ring filled by direct global->LDS copies
+// that 2 producer waves issue and wait for, so the consumers never stall on
+// the memory pipeline; each query block is itself a ring item, so the ring
+// never drains at a job change.
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -26,158 +41,335 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D>
 struct DecCfg {
-  static constexpr int ROWS = 128;         // query heads per workgroup
-  static constexpr int BN = 64;            // keys per tile
-  static constexpr int NT = 256;
-  static constexpr int KS = D + 8;
-  static constexpr int VS = D + 32;
-  static constexpr int KT = BN * KS;
-  static constexpr int VT = BN * VS;
-  static constexpr int CPT = BN * D / 8 / NT;
+  static constexpr int ROWS = kDecodeRows;            // query heads per job
+  static constexpr int NWC = 8;                       // consumers: 4 head blocks x 2 step parities
+  static constexpr int NWP = 2;                       // producer waves (copies only)
+  static constexpr int NWT = NWC + NWP;
+  static constexpr int NT = 64 * NWT;
+  static constexpr int BN = 32;                       // keys per ring item
+  using L = TileLayout<D>;
+  static constexpr int GROUPS = BN / L::RG;           // 1 KB copy groups per 32-row tile
+  static constexpr int TB = GROUPS * L::GS;           // bytes of one 32-row tile image
+  static constexpr int SB = 2 * TB;                   // ring item: K then V, or 2 query blocks
+  static constexpr int NS = D == 128 ? 7 : 12;        // ring depth
+  static constexpr int PER = 2 * GROUPS / NWP;        // copies per producer lane per ring item
+  static constexpr int WIN = 512;                     // cache lengths kept in LDS
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
+  static constexpr int MSLOT = 64 * (16 * DBLK + 2);  // floats of one wave's softmax state
+  static constexpr int MSLOTS = D == 128 ? 2 : 4;     // head blocks merged per round
+};
+
+__device__ __forceinline__ int clamp_len(int L, int smax) { return L < 0 ? 0 : (L > smax ? smax : L); }
+
+// Wait until at most PER * k copies of this lane are outstanding.
+template <int PER, int K>
+__device__ __forceinline__ void vm_wait_imm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER * K) : "memory");
+}
+template <int PER, int KMAX>
+__device__ __forceinline__ void wait_items(int k) {
+  static_assert(PER * KMAX <= 63 && KMAX <= 15, "vmcnt range");
+#define ATTN_WAIT_CASE(n) \
+  case n: if constexpr (KMAX >= n) { vm_wait_imm<PER, n>(); break; } [[fallthrough]];
+  switch (k) {
+    ATTN_WAIT_CASE(15)
+    ATTN_WAIT_CASE(14)
+    ATTN_WAIT_CASE(13)
+    ATTN_WAIT_CASE(12)
+    ATTN_WAIT_CASE(11)
+    ATTN_WAIT_CASE(10)
+    ATTN_WAIT_CASE(9)
+    ATTN_WAIT_CASE(8)
+    ATTN_WAIT_CASE(7)
+    ATTN_WAIT_CASE(6)
+    ATTN_WAIT_CASE(5)
+    ATTN_WAIT_CASE(4)
+    ATTN_WAIT_CASE(3)
+    ATTN_WAIT_CASE(2)
+    ATTN_WAIT_CASE(1)
+    default: vm_wait_imm<PER, 0>(); break;
+  }
+#undef ATTN_WAIT_CASE
+}
+
+// Workgroup-wide sum and exclusive prefix of one value per thread.
+template <int NWAVE>
+__device__ __forceinline__ long long block_sum(long long v, long long* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) t += sh[w];
+  __syncthreads();
+  return t;
+}
+template <int NWAVE>
+__device__ __forceinline__ long long block_excl_scan(long long v, long long* sh, long long* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  long long x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  long long off = 0, t = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    off += w < wave ? sh[w] : 0;
+    t += sh[w];
+  }
+  *total = t;
+  __syncthreads();
+  return off + x - v;
+}
+
+// Position in one workgroup's sequence of ring items: job (b, jb) with
+// jb = kv head * nhg + head group, key step `step` of that job; `phase` < nq
+// for the query-block items that open a job's segment, == nq for K/V items.
+struct Cursor {
+  int b, jb, step, phase;
+  int n, Lb, nq, rows, g_kv, hg;  // of the current job
+  int left;                       // K/V steps left in this workgroup's range
 };
 
 template <int D, bool kSoftcap>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeArgs a) {
   using C = DecCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_k[2 * C::KT];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_v[2 * C::VT];
+  using L = typename C::L;
+  __shared__ __attribute__((aligned(16))) char ring[C::NS * C::SB];
+  __shared__ __attribute__((aligned(16))) float mrg[C::MSLOTS * C::MSLOT];
+  __shared__ int win_len[C::WIN];
+  __shared__ long long red[C::NWT];
+  __shared__ long long sh_b0, sh_off0;
 
-  const int split = blockIdx.x;
-  const int b = blockIdx.z;
-  int L = a.seqlens[b];
-  L = L < 0 ? 0 : (L > a.Smax ? a.Smax : L);
-  const int k_begin = split * a.chunk;
-  if (k_begin >= L) return;  // the combine only reads the first ceil(L / chunk) splits
-  const int k_end = min(L, k_begin + a.chunk);
-
-  const int G = a.Hq / a.Hkv;
-  const int nhb = (G + C::ROWS - 1) / C::ROWS;
-  const int g_kv = blockIdx.y / nhb;
-  const int hb = blockIdx.y % nhb;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= C::NWC;
+  const int hb = wave & 3, par = (wave >> 2) & 1;  // consumer head block and step parity
   const int g = lane >> 5, c = lane & 31;
-  const int row = hb * C::ROWS + wave * 32 + c;
-  const bool row_ok = row < G;
-  const int h = g_kv * G + row;
+  const int G = a.Hq / a.Hkv;
+  const int jpb = a.Hkv * a.nhg;  // jobs per sequence
+  const int P = gridDim.x;
+  const int w_id = blockIdx.x;
 
-  const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.q_sb + (int64_t)h * a.q_sh;
-  const bf16_t* kp = static_cast<const bf16_t*>(a.k) + b * a.k_sb + g_kv * a.k_sh;
-  const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.v_sb + g_kv * a.v_sh;
-
-  const float scale_abs = fabsf(a.scale);
-  const uint32_t sign_flip = a.scale < 0.0f ? 0x80008000u : 0u;
-  bf16x8 qf[C::DSTEPS];
-#pragma unroll
-  for (int ds = 0; ds < C::DSTEPS; ++ds) {
-    if (row_ok) {
-      uint4 raw = *reinterpret_cast<const uint4*>(qp + 16 * ds + 8 * g);
-      raw.x ^= sign_flip; raw.y ^= sign_flip; raw.z ^= sign_flip; raw.w ^= sign_flip;
-      qf[ds] = __builtin_bit_cast(bf16x8, raw);
-    } else {
-      uint4 z = make_uint4(0, 0, 0, 0);
-      qf[ds] = __builtin_bit_cast(bf16x8, z);
+  // ---- this workgroup's step range [lo, hi) ----
+  long long S, lo, hi;
+  if (a.B <= C::NT) {  // one pass: every thread keeps its sequence's length
+    const int Lt = tid < a.B ? clamp_len(a.seqlens[tid], a.Smax) : 0;
+    const int n = (Lt + C::BN - 1) / C::BN;
+    const long long pre = block_excl_scan<C::NWT>((long long)n * jpb, red, &S);
+    const int Pe = S < P ? (int)S : P;
+    if (w_id >= Pe) return;
+    lo = (long long)w_id * S / Pe;
+    hi = (long long)(w_id + 1) * S / Pe;
+    if (n > 0 && pre <= lo && lo < pre + (long long)n * jpb) {
+      sh_b0 = tid;
+      sh_off0 = lo - pre;
     }
+    __syncthreads();
+    const int b0 = (int)sh_b0;
+    if (tid >= b0 && tid - b0 < C::WIN) win_len[tid - b0] = Lt;
+    for (int i = tid + (a.B - b0); i < C::WIN; i += C::NT) win_len[i] = 0;
+  } else {
+    S = 0;
+    for (int base = 0; base < a.B; base += C::NT) {
+      const int b = base + tid;
+      const int n = b < a.B ? (clamp_len(a.seqlens[b], a.Smax) + C::BN - 1) / C::BN : 0;
+      S += block_sum<C::NWT>(n, red);
+    }
+    S *= jpb;
+    const int Pe = S < P ? (int)S : P;
+    if (w_id >= Pe) return;
+    lo = (long long)w_id * S / Pe;
+    hi = (long long)(w_id + 1) * S / Pe;
+    long long carry = 0;
+    for (int base = 0; base < a.B; base += C::NT) {
+      const int b = base + tid;
+      const int n = b < a.B ? (clamp_len(a.seqlens[b], a.Smax) + C::BN - 1) / C::BN : 0;
+      long long tot;
+      const long long pre = carry + block_excl_scan<C::NWT>((long long)n * jpb, red, &tot);
+      if (n > 0 && pre <= lo && lo < pre + (long long)n * jpb) {
+        sh_b0 = b;
+        sh_off0 = lo - pre;
+      }
+      carry += tot;
+    }
+    __syncthreads();
+    const int b0 = (int)sh_b0;
+    for (int i = tid; i < C::WIN; i += C::NT)
+      win_len[i] = b0 + i < a.B ? clamp_len(a.seqlens[b0 + i], a.Smax) : 0;
   }
-  const float scale_log2 = scale_abs * kLog2e;
-  const float cap_k2 = kSoftcap ? 2.0f * kLog2e * scale_abs / a.softcap : 0.0f;
-  const float cap_log2 = a.softcap * kLog2e;
+  __syncthreads();
+  const int b0 = (int)sh_b0;
 
-  const int t_begin = k_begin / C::BN;
-  const int ntiles = (k_end - k_begin + C::BN - 1) / C::BN;
+  auto len_of = [&](int b) -> int {
+    return b - b0 < C::WIN ? win_len[b - b0] : clamp_len(a.seqlens[b], a.Smax);
+  };
+  auto set_job = [&](Cursor& cu) {
+    cu.g_kv = cu.jb / a.nhg;
+    cu.hg = cu.jb - cu.g_kv * a.nhg;
+    cu.rows = min(C::ROWS, G - cu.hg * C::ROWS);
+    cu.nq = cu.rows > 64 ? 2 : 1;
+  };
+  auto start = [&](Cursor& cu) {
+    cu.b = b0;
+    cu.Lb = len_of(b0);
+    cu.n = (cu.Lb + C::BN - 1) / C::BN;
+    const int off = (int)sh_off0;
+    cu.jb = off / cu.n;
+    cu.step = off - cu.jb * cu.n;
+    cu.phase = 0;
+    cu.left = (int)(hi - lo);
+    set_job(cu);
+  };
+  auto advance = [&](Cursor& cu) {
+    if (cu.phase < cu.nq) {
+      ++cu.phase;
+      return;
+    }
+    --cu.left;
+    ++cu.step;
+    if (cu.left == 0 || cu.step < cu.n) return;
+    cu.step = 0;
+    cu.phase = 0;
+    if (++cu.jb == jpb) {
+      cu.jb = 0;
+      do {
+        ++cu.b;
+        cu.Lb = len_of(cu.b);
+        cu.n = (cu.Lb + C::BN - 1) / C::BN;
+      } while (cu.n == 0);
+    }
+    set_job(cu);
+  };
 
-  uint4 kr[C::CPT], vr[C::CPT];
-  auto load_regs = [&](int kt) {
+  // ---- producer waves: copy u is copy cpy = p + NWP * u of the item: tile
+  // cpy / GROUPS (0: first tile of the item, 1: second), 1 KB group
+  // cpy % GROUPS; lane l of a group copies row RG * group + l % RG, 16-byte
+  // chunk l / RG.
+  const int pw = producer ? wave - C::NWC : 0;
+
+  auto issue = [&](const Cursor& pc, int slot) {
+    // (Lane constants are recomputed here so that they do not occupy
+    // registers in the consumer waves.)
+    const int lrow = lane % L::RG, cp_chunk = lane / L::RG;
+    char* item = ring + slot * C::SB;
+    if (pc.phase < pc.nq) {  // query heads [64 phase, 64 phase + 64) of the job
+      const char* qb = static_cast<const char*>(a.q) +
+                       ((int64_t)pc.b * a.q_sb + (int64_t)(pc.g_kv * G + pc.hg * C::ROWS) * a.q_sh) * 2;
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int r = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      const int key = kt * C::BN + r;
-      if (key < k_end) {
-        kr[u] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * a.k_ss + col);
-        vr[u] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * a.v_ss + col);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < C::PER; ++u) {
+        const int cpy = pw + C::NWP * u, mat = cpy / C::GROUPS, grp = cpy % C::GROUPS;
+        int r = 64 * pc.phase + 32 * mat + grp * L::RG + lrow;
+        r = r < pc.rows ? r : pc.rows - 1;  // heads past the job's last repeat it (unused)
+        dma16(qb + ((int64_t)r * a.q_sh + cp_chunk * 8) * 2, lds_addr(item + mat * C::TB + grp * L::GS));
+      }
+    } else {
+      const int row0 = pc.step * C::BN;
+      const char* kb = static_cast<const char*>(a.k) +
+                       ((int64_t)pc.b * a.k_sb + (int64_t)pc.g_kv * a.k_sh + (int64_t)row0 * a.k_ss) * 2;
+      const char* vb = static_cast<const char*>(a.v) +
+                       ((int64_t)pc.b * a.v_sb + (int64_t)pc.g_kv * a.v_sh + (int64_t)row0 * a.v_ss) * 2;
+      if (row0 + C::BN <= pc.Lb) {
+        const int64_t koff = ((int64_t)lrow * a.k_ss + cp_chunk * 8) * 2;  // bytes, from a group's first row
+        const int64_t voff = ((int64_t)lrow * a.v_ss + cp_chunk * 8) * 2;
+#pragma unroll
+        for (int u = 0; u < C::PER; ++u) {
+          const int cpy = pw + C::NWP * u, mat = cpy / C::GROUPS, grp = cpy % C::GROUPS;
+          const char* src = mat ? vb + (int64_t)grp * L::RG * a.v_ss * 2 + voff
+                                : kb + (int64_t)grp * L::RG * a.k_ss * 2 + koff;
+          dma16(src, lds_addr(item + mat * C::TB + grp * L::GS));
+        }
+      } else {  // the job's last step: rows past the cache length repeat the last one
+#pragma unroll
+        for (int u = 0; u < C::PER; ++u) {
+          const int cpy = pw + C::NWP * u, mat = cpy / C::GROUPS, grp = cpy % C::GROUPS;
+          int r = grp * L::RG + lrow;
+          r = row0 + r < pc.Lb ? r : pc.Lb - 1 - row0;
+          const int64_t ld = mat ? a.v_ss : a.k_ss;
+          dma16((mat ? vb : kb) + ((int64_t)r * ld + cp_chunk * 8) * 2, lds_addr(item + mat * C::TB + grp * L::GS));
+        }
       }
     }
   };
-  auto store_regs = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int r = chunk / (D / 8);
-      const int col = (chunk % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(lds_k + buf * C::KT + r * C::KS + col) = kr[u];
-      *reinterpret_cast<uint4*>(lds_v + buf * C::VT + r * C::VS + col) = vr[u];
-    }
-  };
 
-  float m_run = kNegInf, l_run = 0.0f;
+  // ---- consumer state: this wave's 32 heads over its parity's steps ----
+  // Scores are raw dot products; the scale is applied inside exp2 (the query
+  // is negated for a negative scale, so the applied scale is positive).
+  const float scl = fabsf(a.scale) * kLog2e;
+  const uint32_t qsign = a.scale < 0.0f ? 0x80008000u : 0u;
+  const float cap_k2 = kSoftcap ? 2.0f * kLog2e * fabsf(a.scale) / a.softcap : 0.0f;
+  const float cap_log2 = a.softcap * kLog2e;
+  const int beta = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
+  const int tr_chunk = 2 * (beta & 1) + ((s16 & 3) >> 1);
+  const int tr_half = 8 * (s16 & 1);
+
+  bf16x8 qf[C::DSTEPS];
+  float m_run = kNegInf, l_run = 0.0f;  // m_run in exp2 units
   f32x16 oacc[C::DBLK];
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) qf[ds] = bf16x8{};
 #pragma unroll
   for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
-  load_regs(t_begin);
-  store_regs(0);
-  __syncthreads();
-
-  const int beta = lane >> 4, s16 = lane & 15;
-  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
-  const int tr_col = 16 * (beta & 1) + 4 * (s16 & 3);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kt = t_begin + t;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_regs(kt + 1);
-
-    const bf16_t* kb_base = lds_k + buf * C::KT;
-    f32x16 sacc[2];
+  // One group of NI (1 or 2) consecutive K/V steps of the job for this
+  // wave's 32 heads; the steps' score tiles are independent matrix-core
+  // chains and share one max / rescale.
+  auto kv_group = [&](auto ni_tag, int i0, int step, int Lb) {
+    constexpr int NI = decltype(ni_tag)::value;
+    f32x16 sacc[NI];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < NI; ++t) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb_base + (32 * kb + c) * C::KS + 16 * ds + 8 * g);
-        sacc[kb] = mfma32(ka, qf[ds], sacc[kb]);
-      }
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
     }
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const char* kt = ring + ((i0 + t) % C::NS) * C::SB;
+      bf16x8 ka[C::DSTEPS];
+#pragma unroll
+      for (int ds = 0; ds < C::DSTEPS; ++ds)
+        ka[ds] = *reinterpret_cast<const bf16x8*>(kt + L::off(c, 2 * ds + g));
+#pragma unroll
+      for (int ds = 0; ds < C::DSTEPS; ++ds) sacc[t] = mfma32(ka[ds], qf[ds], sacc[t]);
+    }
+    // sacc[t][r]: key 8*(r/4) + 4*g + r%4 of step step + t, head c.  Keys
+    // past the cache length hold copies of the last key, so they never
+    // raise the max.
     if (kSoftcap) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int t = 0; t < NI; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(sacc[kb][r] * cap_k2);
-          sacc[kb][r] = cap_log2 * (1.0f - 2.0f * fast_rcp(e + 1.0f));
+          const float e = fast_exp2(sacc[t][r] * cap_k2);
+          sacc[t][r] = cap_log2 * (1.0f - 2.0f * fast_rcp(e + 1.0f));
         }
     }
-    const int key0 = kt * C::BN + 4 * g;
-    if (kt * C::BN + C::BN > k_end) {
+    // (Plain fmaxf here: the matrix-core results must be read by compiled
+    // instructions, which get the MFMA -> VALU wait states.)
+    float mt[NI];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < NI; ++t) {
+      float m4[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + 32 * kb + 8 * (r >> 2) + (r & 3) >= k_end) sacc[kb][r] = kNegInf;
+      for (int q = 0; q < 4; ++q)
+        m4[q] = fmaxf(fmaxf(sacc[t][4 * q], sacc[t][4 * q + 1]), fmaxf(sacc[t][4 * q + 2], sacc[t][4 * q + 3]));
+      mt[t] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     }
-
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float mx2 = kSoftcap ? mx : mx * scale_log2;
-    if (__any(mx2 > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, mx2);
+    float mx = NI == 2 ? fmaxf(mt[0], mt[NI - 1]) : mt[0];
+    mx = pair_max32(mx);
+    if (!kSoftcap) mx *= scl;
+    if (__any(mx > m_run + 8.0f)) {
+      const float m_new = max_nc(m_run, mx);
       const float alpha = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -186,109 +378,274 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
     }
-    const float msub = (m_run == kNegInf) ? 0.0f : m_run;
-    bf16x8 pf[2][2];
-    float ls = 0.0f;
+    bf16x8 pf[NI][2];
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < NI; ++t) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p[r] = kSoftcap ? fast_exp2(sacc[t][r] - m_run) : fast_exp2(__builtin_fmaf(sacc[t][r], scl, -m_run));
+      if ((step + t + 1) * C::BN > Lb) {
+        const int key0 = (step + t) * C::BN + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = key0 + 8 * (r >> 2) + (r & 3) < Lb ? p[r] : 0.0f;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = kSoftcap ? fast_exp2(sacc[kb][r] - msub)
-                                 : fast_exp2(__builtin_fmaf(sacc[kb][r], scale_log2, -msub));
-        ls += p;
-        pf[kb][r >> 3][r & 7] = static_cast<__bf16>(p);
+        ls[r & 3] += p[r];
+        pf[t][r >> 3][r & 7] = static_cast<__bf16>(p[r]);
       }
-    l_run += ls;
-
-    const bf16_t* vb_base = lds_v + buf * C::VT;
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < C::DBLK; ++db)
+    for (int t = 0; t < NI; ++t) {
+      const char* vt = ring + ((i0 + t) % C::NS) * C::SB + C::TB;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 va[C::DBLK];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16_t* p0 = vb_base + (32 * kb + 16 * ks + tr_row) * C::VS + 32 * db + tr_col;
-          const i16x4 lo = lds_read_tr16(p0);
-          const i16x4 hi = lds_read_tr16(p0 + 8 * C::VS);
-          const bf16x8 va = cat_frag(lo, hi);
-          oacc[db] = mfma32(va, pf[kb][ks], oacc[db]);
+        for (int db = 0; db < C::DBLK; ++db) {
+          const char* p0 = vt + L::off(16 * ks + tr_row, 4 * db + tr_chunk) + tr_half;
+          const char* p1 = vt + L::off(16 * ks + 8 + tr_row, 4 * db + tr_chunk) + tr_half;
+          va[db] = cat_frag(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+                            lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
         }
-
-    if (has_next) store_regs(buf ^ 1);
-    __syncthreads();
-  }
-
-  const float l_tot = l_run + wave_xor32(l_run);
-  if (row_ok) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* op = a.part_o + (((int64_t)b * a.max_splits + split) * a.Hq + h) * D;
 #pragma unroll
-    for (int db = 0; db < C::DBLK; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float4 v4 = make_float4(oacc[db][4 * rr] * inv, oacc[db][4 * rr + 1] * inv,
-                                oacc[db][4 * rr + 2] * inv, oacc[db][4 * rr + 3] * inv);
-        *reinterpret_cast<float4*>(op + 32 * db + 8 * rr + 4 * g) = v4;
+        for (int db = 0; db < C::DBLK; ++db) oacc[db] = mfma32(va[db], pf[t][ks], oacc[db]);
       }
-    if (g == 0)
-      a.part_lse[((int64_t)b * a.max_splits + split) * a.Hq + h] =
-          l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+  };
+
+  // End of this workgroup's segment of job (cc.b, cc.jb): parity 1 hands its
+  // softmax state to parity 0 through LDS, and parity 0 writes the merged
+  // partial result (normalised O in fp32, natural-log LSE) to slot w + j.
+  // Every wave takes part in the barriers.
+  auto finish_segment = [&](const Cursor& cc, bool job_end) {
+    const bool active = !producer && hb * 32 < cc.rows;
+    const int64_t j = (int64_t)cc.b * jpb + cc.jb;
+    const int64_t slot = w_id + j;
+#pragma unroll
+    for (int round = 0; round < 4 / C::MSLOTS; ++round) {
+      const bool mine = active && hb / C::MSLOTS == round;
+      float* ms = mrg + (hb % C::MSLOTS) * C::MSLOT;
+      if (round > 0) __syncthreads();  // the previous round's readers are done
+      if (mine && par == 1) {
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            *reinterpret_cast<float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4) =
+                make_float4(oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]);
+        ms[16 * C::DBLK * 64 + lane] = m_run;
+        ms[16 * C::DBLK * 64 + 64 + lane] = l_run;
+      }
+      __syncthreads();
+      if (mine && par == 0) {
+        const float mo = ms[16 * C::DBLK * 64 + lane];
+        const float lo1 = ms[16 * C::DBLK * 64 + 64 + lane];
+        const float M = fmaxf(m_run, mo);
+        const float a0 = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
+        const float a1 = mo == kNegInf ? 0.0f : fast_exp2(mo - M);
+        const float l_tot = pair_sum32(l_run * a0 + lo1 * a1);
+        const int row = hb * 32 + c;
+        if (row < cc.rows) {
+          const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+          const float s0 = a0 * inv, s1 = a1 * inv;
+          float* op = a.part_o + (slot * C::ROWS + row) * D;
+#pragma unroll
+          for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const float4 o1 = *reinterpret_cast<const float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4);
+              const float4 v4 =
+                  make_float4(oacc[db][4 * rr] * s0 + o1.x * s1, oacc[db][4 * rr + 1] * s0 + o1.y * s1,
+                              oacc[db][4 * rr + 2] * s0 + o1.z * s1, oacc[db][4 * rr + 3] * s0 + o1.w * s1);
+              *reinterpret_cast<float4*>(op + 32 * db + 8 * rr + 4 * g) = v4;
+            }
+          if (g == 0)
+            a.part_lse[slot * C::ROWS + row] = l_tot > 0.0f ? (M + fast_log2(l_tot)) * kLn2 : kNegInf;
+        }
+      }
+    }
+    if (tid == 0 && job_end) a.job_seg[2 * j + 1] = w_id;  // this workgroup ends the job
+  };
+
+  // ---- the ring: item i lives in slot i % NS.  Producer waves issue the
+  // copies and wait for them; the barrier of each group hands the group's
+  // items to the consumer waves and the slots of earlier groups back to the
+  // producers. ----
+  using One = std::integral_constant<int, 1>;
+  Cursor cc;
+  start(cc);
+  Cursor pc = cc;
+  int issued = 0;
+  if (producer) {
+    for (; issued < C::NS && pc.left > 0; ++issued) {
+      issue(pc, issued);
+      advance(pc);
+    }
+  }
+  for (int i = 0; cc.left > 0;) {
+    // The next group: a job's query items, or up to two K/V steps of a job.
+    const bool qgrp = cc.phase < cc.nq;
+    const int gsz = qgrp ? cc.nq : ((cc.left >= 2 && cc.step + 1 < cc.n) ? 2 : 1);
+    if (producer) wait_items<C::PER, C::NS - 1>(issued - (i + gsz));
+    __syncthreads();  // the group is in LDS; slots of earlier items are free
+    if (producer) {
+      while (pc.left > 0 && issued < i + C::NS) {
+        issue(pc, issued % C::NS);
+        advance(pc);
+        ++issued;
+      }
+    } else if (qgrp) {
+      if (tid == 0 && cc.step == 0)  // this workgroup starts the job
+        a.job_seg[2 * ((int64_t)cc.b * jpb + cc.jb)] = w_id;
+      m_run = kNegInf;
+      l_run = 0.0f;
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+      if (hb * 32 < cc.rows) {
+        const char* qt = ring + ((i + (hb >> 1)) % C::NS) * C::SB + (hb & 1) * C::TB;
+#pragma unroll
+        for (int ds = 0; ds < C::DSTEPS; ++ds) {
+          uint4 raw = *reinterpret_cast<const uint4*>(qt + L::off(c, 2 * ds + g));
+          raw.x ^= qsign;
+          raw.y ^= qsign;
+          raw.z ^= qsign;
+          raw.w ^= qsign;
+          qf[ds] = __builtin_bit_cast(bf16x8, raw);
+        }
+      }
+    } else if (par < gsz && hb * 32 < cc.rows) {
+      kv_group(One{}, i + par, cc.step + par, cc.Lb);
+    }
+    if (!qgrp) {
+      const bool job_end = cc.step + gsz == cc.n;
+      if (job_end || cc.left == gsz) finish_segment(cc, job_end);
+    }
+    for (int t = 0; t < gsz; ++t) advance(cc);
+    i += gsz;
   }
 }
 
-// One thread per (head, d): merge the splits of one sequence.
+// Merge the partial results of one job: one thread per (head row, 4 columns).
+// The job's partials are in slots w + j for w from its first to its last
+// workgroup, as recorded by the split kernel.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int HPB = 256 / D;  // heads per block
-  const int b = blockIdx.y;
-  const int h = blockIdx.x * HPB + threadIdx.x / D;
-  const int d = threadIdx.x % D;
-  if (h >= a.Hq) return;
-  int L = a.seqlens[b];
-  L = L < 0 ? 0 : (L > a.Smax ? a.Smax : L);
-  const int n = (L + a.chunk - 1) / a.chunk;
-  const float* pl = a.part_lse + (int64_t)b * a.max_splits * a.Hq + h;
-  const float* po = a.part_o + ((int64_t)b * a.max_splits * a.Hq + h) * D + d;
-  float m = kNegInf;
-  for (int s = 0; s < n; ++s) m = fmaxf(m, pl[(int64_t)s * a.Hq]);
-  float tot = 0.0f, acc = 0.0f;
-  if (m != kNegInf) {
-    for (int s = 0; s < n; ++s) {
-      const float ls = pl[(int64_t)s * a.Hq];
-      const float w = ls == kNegInf ? 0.0f : fast_exp2((ls - m) * kLog2e);
-      tot += w;
-      acc = __builtin_fmaf(w, po[(int64_t)s * a.Hq * D], acc);
+  constexpr int TPH = D / 4;      // threads per head
+  constexpr int HPB = 256 / TPH;  // heads per workgroup
+  constexpr int ROWS = DecCfg<D>::ROWS;
+  constexpr int U = 8;            // partials loaded per round
+  const int j = blockIdx.x;
+  const int jpb = a.Hkv * a.nhg;
+  const int b = j / jpb, jb = j % jpb;
+  const int g_kv = jb / a.nhg, hg = jb % a.nhg;
+  const int G = a.Hq / a.Hkv;
+  const int rows = min(ROWS, G - hg * ROWS);
+  const int r = blockIdx.y * HPB + threadIdx.x / TPH;
+  if (r >= rows) return;
+  const int d4 = threadIdx.x % TPH;
+  const int h = g_kv * G + hg * ROWS + r;
+  const int Lb = clamp_len(a.seqlens[b], a.Smax);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float m = kNegInf, tot = 0.0f;
+  if (Lb > 0) {
+    const int w0 = a.job_seg[2 * j], w1 = a.job_seg[2 * j + 1];
+    const float* pl = a.part_lse + ((int64_t)w0 + j) * ROWS + r;
+    const float* po = a.part_o + (((int64_t)w0 + j) * ROWS + r) * D + 4 * d4;
+    const int ns = w1 - w0 + 1;
+    for (int s0 = 0; s0 < ns; s0 += U) {
+      float ls[U];
+      float4 ov[U];
+#pragma unroll
+      for (int e = 0; e < U; ++e) {
+        const bool ok = s0 + e < ns;
+        ls[e] = ok ? pl[(int64_t)(s0 + e) * ROWS] : kNegInf;
+        ov[e] = ok ? *reinterpret_cast<const float4*>(po + (int64_t)(s0 + e) * ROWS * D)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float mr = m;
+#pragma unroll
+      for (int e = 0; e < U; ++e) mr = fmaxf(mr, ls[e]);
+      if (mr == kNegInf) continue;
+      const float sc = m == kNegInf ? 0.0f : fast_exp2((m - mr) * kLog2e);
+      tot *= sc;
+      acc.x *= sc;
+      acc.y *= sc;
+      acc.z *= sc;
+      acc.w *= sc;
+#pragma unroll
+      for (int e = 0; e < U; ++e) {
+        const float wgt = ls[e] == kNegInf ? 0.0f : fast_exp2((ls[e] - mr) * kLog2e);
+        tot += wgt;
+        acc.x = __builtin_fmaf(wgt, ov[e].x, acc.x);
+        acc.y = __builtin_fmaf(wgt, ov[e].y, acc.y);
+        acc.z = __builtin_fmaf(wgt, ov[e].z, acc.z);
+        acc.w = __builtin_fmaf(wgt, ov[e].w, acc.w);
+      }
+      m = mr;
     }
   }
-  bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)h * a.o_sh;
-  op[d] = f32_to_bf16(tot > 0.0f ? acc / tot : 0.0f);
-  if (d == 0) a.lse[(int64_t)b * a.Hq + h] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
+  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+  bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)h * a.o_sh + 4 * d4;
+  const uint32_t lo2 = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.x * inv)) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.y * inv)) << 16);
+  const uint32_t hi2 = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.z * inv)) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.w * inv)) << 16);
+  *reinterpret_cast<uint2*>(op) = make_uint2(lo2, hi2);
+  if (d4 == 0) a.lse[(int64_t)b * a.Hq + h] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int nhb = (G + DecCfg<D>::ROWS - 1) / DecCfg<D>::ROWS;
-  const dim3 grid(a.max_splits, a.Hkv * nhb, a.B);
-  if (a.softcap > 0.0f) hipLaunchKernelGGL((decode_split_kernel<D, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decode_split_kernel<D, false>), grid, dim3(256), 0, s, a);
+  const dim3 block(DecCfg<D>::NT);
+  if (a.softcap > 0.0f) hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(a.parts), block, 0, s, a);
+  else hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(a.parts), block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int HPB = 256 / D;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((a.Hq + HPB - 1) / HPB, a.B), dim3(256), 0, s, a);
+  constexpr int HPB = 256 / (D / 4);
+  const int jobs = a.B * a.Hkv * a.nhg;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(jobs, (DecCfg<D>::ROWS + HPB - 1) / HPB), dim3(256),
+                     0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int Hq, int D, int max_splits) {
-  const size_t o = ((size_t)B * max_splits * Hq * D * sizeof(float) + 255) / 256 * 256;
-  const size_t l = ((size_t)B * max_splits * Hq * sizeof(float) + 255) / 256 * 256;
-  return o + l;
+int decode_head_groups(int Hq, int Hkv) { return (Hq / Hkv + kDecodeRows - 1) / kDecodeRows; }
+
+int decode_parts(int num_splits) {
+  if (num_splits > 0) return num_splits;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int D, int parts) {
+  DecodeWorkspace w;
+  const size_t jobs = (size_t)B * Hkv * decode_head_groups(Hq, Hkv);
+  const size_t slots = (size_t)parts + jobs;
+  w.o_off = 0;
+  w.lse_off = (slots * kDecodeRows * D * sizeof(float) + 255) / 256 * 256;
+  w.seg_off = w.lse_off + (slots * kDecodeRows * sizeof(float) + 255) / 256 * 256;
+  w.bytes = w.seg_off + (jobs * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  return w;
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
-  if (a.B == 0 || a.max_splits == 0) return hipSuccess;
+  if (a.B == 0) return hipSuccess;
   if (a.D == 64) return launch_d<64>(a, s);
   return launch_d<128>(a, s);
 }

@@ -94,12 +94,20 @@ struct DecodeArgs {
   int B, Hq, Hkv, D, Smax;
   float scale;
   float softcap;
-  int chunk;                 // keys per split
-  int max_splits;            // splits per sequence (grid extent)
-  float* part_o;             // workspace [B, max_splits, Hq, D]
-  float* part_lse;           // workspace [B, max_splits, Hq]
+  int parts;                 // workgroups; the key work is cut into this many equal ranges
+  int nhg;                   // groups of up to kDecodeRows query heads per kv head
+  float* part_o;             // workspace [parts + jobs][kDecodeRows][D]
+  float* part_lse;           // workspace [parts + jobs][kDecodeRows]
+  int32_t* job_seg;          // workspace [jobs][2]: first and last workgroup of each job
 };
-size_t decode_workspace_bytes(int B, int Hq, int D, int max_splits);
+constexpr int kDecodeRows = 128;  // query heads per decode job
+// Number of workgroups: num_splits when > 0, else the device's compute units.
+int decode_parts(int num_splits);
+int decode_head_groups(int Hq, int Hkv);
+struct DecodeWorkspace {
+  size_t o_off, lse_off, seg_off, bytes;
+};
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int D, int parts);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
 struct BlockMaskArgs {

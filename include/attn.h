@@ -218,10 +218,11 @@ attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
 /* ---------------------------------------------------------------------
  * Decode over a KV cache ([FA] flash_attn_with_kvcache: q attends to the
  * first cache_seqlens[b] rows of its batch row of k_cache / v_cache; no
- * backward).  Split-K: each sequence's cache prefix is cut into chunks that
- * are attended independently, and the chunk results are merged with the
- * LSE-weighted combine  lse = log sum_s exp(lse_s),
- * o = sum_s exp(lse_s - lse) o_s.
+ * backward).  Split-K: the keys of every (sequence, kv head, group of up to
+ * 128 query heads) job, in 32-key steps and job order, are cut into equal
+ * contiguous ranges, one per workgroup; the pieces are attended
+ * independently and merged with the LSE-weighted combine
+ * lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.
  *   p : B, Sq (== 1), Hq, Hkv, D as usual; Sk = cache capacity Smax;
  *       scale and softcap apply; causal, window, ALiBi and block masks are
  *       not supported by this entry point (UNSUPPORTED).
@@ -229,8 +230,9 @@ attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
  *   cache_seqlens : device int32 [B], each in [0, Smax] (values outside are
  *       clamped to that range on the device).  A sequence of length 0 gives
  *       o = 0 and lse = -inf.
- *   num_splits : keys per split is chosen by the library when 0; otherwise
- *       the maximum number of splits per sequence (>= 1).
+ *   num_splits : number of ranges (workgroups) the total key work is cut
+ *       into; 0 = one per compute unit of the current device.  At most
+ *       65536.  Any value gives the same result up to rounding.
  *   o : [B, 1, Hq, D];  lse : fp32 [B, Hq, 1] contiguous.
  *   workspace : at least attn_decode_workspace_size(p, num_splits) bytes.
  */

@@ -37,7 +37,7 @@ def test_decode_mqa_full(b):
     w = inputs.decode_mqa()
     O, L = oracle.decode(f64(w, "q"), f64(w, "k"), f64(w, "v"), w["cache_seqlens"],
                          scale=w["scale"])
-    for splits in (0, 3, 40):
+    for splits in (0, 1, 3, 40, 5000):
         o, lse = run_decode(b, w, softmax_scale=w["scale"], num_splits=splits)
         check_o(to_f64(o), O, what="O(splits=%d)" % splits)
         check_lse(to_f64(lse), L)
@@ -48,10 +48,13 @@ def test_decode_mqa_full(b):
     dict(B=2, Hq=256, Hkv=1, D=128, Smax=300, lens=[300, 129]),
     dict(B=4, Hq=16, Hkv=16, D=128, Smax=200, lens=[0, 64, 65, 199]),
     dict(B=2, Hq=40, Hkv=8, D=64, Smax=1000, lens=[999, 1000], softcap=3.0),
+    dict(B=600, Hq=8, Hkv=8, D=64, Smax=40, lens="random"),
+    dict(B=3, Hq=320, Hkv=1, D=128, Smax=100, lens=[100, 1, 33]),
 ])
 def test_decode_ragged(b, cfg):
-    """Ragged cache lengths (1, tile edges, an empty cache), GQA groups that
-    do not fill a 128-row tile, softcap."""
+    """Ragged cache lengths (1, tile edges, empty caches), GQA groups that
+    do not fill a 128-head job or span several, softcap, one workgroup over
+    hundreds of sequences, more workgroups than key steps."""
     w = inputs.decode_mqa(seed=11, B=cfg["B"], Hq=cfg["Hq"], Smax=cfg["Smax"], D=cfg["D"],
                           lmin=1, lmax=cfg["Smax"])
     if cfg["Hkv"] > 1:
@@ -59,9 +62,12 @@ def test_decode_ragged(b, cfg):
         shape = (cfg["B"], cfg["Smax"], cfg["Hkv"], cfg["D"])
         w["k"] = inputs.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
         w["v"] = inputs.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
-    w["cache_seqlens"] = np.array(cfg["lens"], dtype=np.int32)
+    if cfg["lens"] == "random":  # many short caches, some empty: one workgroup spans hundreds
+        w["cache_seqlens"] = np.random.default_rng(13).integers(0, cfg["Smax"] + 1, cfg["B"]).astype(np.int32)
+    else:
+        w["cache_seqlens"] = np.array(cfg["lens"], dtype=np.int32)
     cap = cfg.get("softcap", 0.0)
-    for splits in (0, 1, 7):
+    for splits in (0, 1, 7, 65536):
         o, lse = run_decode(b, w, softmax_scale=0.1, softcap=cap, num_splits=splits)
         O, L = oracle.decode(f64(w, "q"), f64(w, "k"), f64(w, "v"), w["cache_seqlens"],
                              scale=0.1, softcap=cap)
