@@ -23,7 +23,7 @@ Besides the headline line the JSON carries:
                 same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--copy-calibration]
 """
 
 import argparse
@@ -47,7 +47,24 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (256 MiB read, 256 MiB "
+                         "written per launch), the reference for HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain elementwise copy (dst = src * 1) of 256 MiB, five launches: the
+    known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 64 << 20  # fp32 elements = 256 MiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": 4 * n,
+                                           "bytes_written_per_launch": 4 * n, "launches": 5}}))
 
 
 class Prepared:
@@ -87,6 +104,9 @@ def traffic_for(kernel, src_hash, per_launch_units):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU; runs on %d GPUs are not part of this benchmark "
               "(the kernels shard by batch and kv head with no communication)" % args.gpus,
