@@ -27,7 +27,8 @@
 // tiles stream through an NS-deep LDS ring filled by direct global->LDS copies
 // that 2 producer waves issue and wait for, so the consumers never stall on
 // the memory pipeline; each query block is itself a ring item, so the ring
-// never drains at a job change.
+// never drains at a job change.  The hand-over uses LDS counters, not
+// barriers: producers and consumers each run at their own pace.
 
 #include <type_traits>
 
@@ -51,14 +52,32 @@ struct DecCfg {
   static constexpr int GROUPS = BN / L::RG;           // 1 KB copy groups per 32-row tile
   static constexpr int TB = GROUPS * L::GS;           // bytes of one 32-row tile image
   static constexpr int SB = 2 * TB;                   // ring item: K then V, or 2 query blocks
-  static constexpr int NS = D == 128 ? 7 : 12;        // ring depth
+  static constexpr int NS = D == 128 ? 5 : 9;         // ring depth
+  static constexpr int DEPTH = NS - 1;                // items a producer keeps unpublished in flight
   static constexpr int PER = 2 * GROUPS / NWP;        // copies per producer lane per ring item
   static constexpr int WIN = 512;                     // cache lengths kept in LDS
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   static constexpr int MSLOT = 64 * (16 * DBLK + 2);  // floats of one wave's softmax state
-  static constexpr int MSLOTS = D == 128 ? 2 : 4;     // head blocks merged per round
 };
+
+// Bounded spin on an LDS flag: the waves of a workgroup hand items over with
+// counters instead of barriers.  The bound (about 2^22 sleeps) only matters if
+// the protocol were broken; it keeps every wave finite.
+constexpr int kSpinLimit = 1 << 22;
+template <typename Pred>
+__device__ __forceinline__ void spin_until(Pred pred) {
+  for (int n = 0; !pred() && n < kSpinLimit; ++n) __builtin_amdgcn_s_sleep(1);
+}
+__device__ __forceinline__ int lds_acquire(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void publish(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void spin_until_ge(const int* p, int v) {
+  spin_until([&] { return lds_acquire(p) >= v; });
+}
 
 __device__ __forceinline__ int clamp_len(int L, int smax) { return L < 0 ? 0 : (L > smax ? smax : L); }
 
@@ -143,9 +162,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   using C = DecCfg<D>;
   using L = typename C::L;
   __shared__ __attribute__((aligned(16))) char ring[C::NS * C::SB];
-  __shared__ __attribute__((aligned(16))) float mrg[C::MSLOTS * C::MSLOT];
+  __shared__ __attribute__((aligned(16))) float mrg[4 * C::MSLOT];
   __shared__ int win_len[C::WIN];
   __shared__ long long red[C::NWT];
+  __shared__ int landed[C::NWP];       // items whose copies by producer p have landed
+  __shared__ int consumed[C::NWC];     // items consumer wave w is done with
+  __shared__ int mrg_written[4], mrg_read[4];  // merge handshakes per head block
   __shared__ long long sh_b0, sh_off0;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -205,8 +227,26 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     for (int i = tid; i < C::WIN; i += C::NT)
       win_len[i] = b0 + i < a.B ? clamp_len(a.seqlens[b0 + i], a.Smax) : 0;
   }
+  if (tid < C::NWP) landed[tid] = 0;
+  if (tid < C::NWC) consumed[tid] = 0;
+  if (tid < 4) mrg_written[tid] = mrg_read[tid] = 0;
   __syncthreads();
   const int b0 = (int)sh_b0;
+  // Minimum of a group of counters: relaxed loads issued together, then one
+  // acquire fence (an acquire per load would serialise the LDS round trips).
+  auto counters_min = [&](const int* cnt, auto n_tag) {
+    constexpr int N = decltype(n_tag)::value;
+    int v[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) v[q] = __hip_atomic_load(&cnt[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int m = v[0];
+#pragma unroll
+    for (int q = 1; q < N; ++q) m = min(m, v[q]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return m;
+  };
+  auto landed_min = [&]() { return counters_min(landed, std::integral_constant<int, C::NWP>{}); };
+  auto consumed_min = [&]() { return counters_min(consumed, std::integral_constant<int, C::NWC>{}); };
 
   auto len_of = [&](int b) -> int {
     return b - b0 < C::WIN ? win_len[b - b0] : clamp_len(a.seqlens[b], a.Smax);
@@ -418,20 +458,20 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     }
   };
 
-  // End of this workgroup's segment of job (cc.b, cc.jb): parity 1 hands its
-  // softmax state to parity 0 through LDS, and parity 0 writes the merged
-  // partial result (normalised O in fp32, natural-log LSE) to slot w + j.
-  // Every wave takes part in the barriers.
-  auto finish_segment = [&](const Cursor& cc, bool job_end) {
-    const bool active = !producer && hb * 32 < cc.rows;
+  // End of this wave's segment of job (cc.b, cc.jb), number `seg` of this
+  // workgroup: the parity-1 wave of each head block hands its softmax state
+  // to the parity-0 wave through its LDS slot (sequence flags, no barrier),
+  // and the parity-0 wave writes the merged partial result (normalised O in
+  // fp32, natural-log LSE) to slot w + j.  Waves whose head block has no
+  // query heads in this job still step the flags.
+  auto finish_segment = [&](const Cursor& cc, bool job_end, int seg) {
+    const bool active = hb * 32 < cc.rows;
     const int64_t j = (int64_t)cc.b * jpb + cc.jb;
     const int64_t slot = w_id + j;
-#pragma unroll
-    for (int round = 0; round < 4 / C::MSLOTS; ++round) {
-      const bool mine = active && hb / C::MSLOTS == round;
-      float* ms = mrg + (hb % C::MSLOTS) * C::MSLOT;
-      if (round > 0) __syncthreads();  // the previous round's readers are done
-      if (mine && par == 1) {
+    float* ms = mrg + hb * C::MSLOT;
+    if (par == 1) {
+      spin_until_ge(&mrg_read[hb], seg);  // the previous segment's state has been taken
+      if (active) {
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
@@ -441,66 +481,96 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
         ms[16 * C::DBLK * 64 + lane] = m_run;
         ms[16 * C::DBLK * 64 + 64 + lane] = l_run;
       }
-      __syncthreads();
-      if (mine && par == 0) {
-        const float mo = ms[16 * C::DBLK * 64 + lane];
-        const float lo1 = ms[16 * C::DBLK * 64 + 64 + lane];
-        const float M = fmaxf(m_run, mo);
-        const float a0 = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
-        const float a1 = mo == kNegInf ? 0.0f : fast_exp2(mo - M);
-        const float l_tot = pair_sum32(l_run * a0 + lo1 * a1);
-        const int row = hb * 32 + c;
-        if (row < cc.rows) {
-          const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-          const float s0 = a0 * inv, s1 = a1 * inv;
-          float* op = a.part_o + (slot * C::ROWS + row) * D;
-#pragma unroll
-          for (int db = 0; db < C::DBLK; ++db)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const float4 o1 = *reinterpret_cast<const float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4);
-              const float4 v4 =
-                  make_float4(oacc[db][4 * rr] * s0 + o1.x * s1, oacc[db][4 * rr + 1] * s0 + o1.y * s1,
-                              oacc[db][4 * rr + 2] * s0 + o1.z * s1, oacc[db][4 * rr + 3] * s0 + o1.w * s1);
-              *reinterpret_cast<float4*>(op + 32 * db + 8 * rr + 4 * g) = v4;
-            }
-          if (g == 0)
-            a.part_lse[slot * C::ROWS + row] = l_tot > 0.0f ? (M + fast_log2(l_tot)) * kLn2 : kNegInf;
-        }
-      }
+      if (lane == 0) publish(&mrg_written[hb], seg + 1);
+      return;
     }
-    if (tid == 0 && job_end) a.job_seg[2 * j + 1] = w_id;  // this workgroup ends the job
+    spin_until_ge(&mrg_written[hb], seg + 1);
+    if (active) {
+      const float mo = ms[16 * C::DBLK * 64 + lane];
+      const float lo1 = ms[16 * C::DBLK * 64 + 64 + lane];
+      const float M = fmaxf(m_run, mo);
+      const float a0 = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
+      const float a1 = mo == kNegInf ? 0.0f : fast_exp2(mo - M);
+      const float l_tot = pair_sum32(l_run * a0 + lo1 * a1);
+      const int row = hb * 32 + c;
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      const float s0 = a0 * inv, s1 = a1 * inv;
+      float* op = a.part_o + (slot * C::ROWS + row) * D;
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 x = *reinterpret_cast<const float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4);
+          const float4 v4 = make_float4(oacc[db][4 * rr] * s0 + x.x * s1, oacc[db][4 * rr + 1] * s0 + x.y * s1,
+                                        oacc[db][4 * rr + 2] * s0 + x.z * s1, oacc[db][4 * rr + 3] * s0 + x.w * s1);
+          if (row < cc.rows) *reinterpret_cast<float4*>(op + 32 * db + 8 * rr + 4 * g) = v4;
+        }
+      if (g == 0 && row < cc.rows)
+        a.part_lse[slot * C::ROWS + row] = l_tot > 0.0f ? (M + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+    if (lane == 0) publish(&mrg_read[hb], seg + 1);  // the slot may be refilled
+    if (lane == 0 && hb == 0 && job_end) a.job_seg[2 * j + 1] = w_id;  // this workgroup ends the job
   };
 
-  // ---- the ring: item i lives in slot i % NS.  Producer waves issue the
-  // copies and wait for them; the barrier of each group hands the group's
-  // items to the consumer waves and the slots of earlier groups back to the
-  // producers. ----
+  // ---- the ring: item i lives in slot i % NS.  No barriers: the producer
+  // waves publish how many items have landed, each consumer wave publishes
+  // how many items it is done with, and a slot is refilled once every
+  // consumer wave is past its previous item. ----
   using One = std::integral_constant<int, 1>;
   Cursor cc;
   start(cc);
-  Cursor pc = cc;
-  int issued = 0;
   if (producer) {
-    for (; issued < C::NS && pc.left > 0; ++issued) {
-      issue(pc, issued);
+    // The producer shares its SIMD with consumer waves; a higher issue
+    // priority keeps its copies flowing while they compute.
+    __builtin_amdgcn_s_setprio(3);
+    Cursor pc = cc;
+    int issued = 0, published = 0;
+    auto publish_all = [&]() {
+      if (published < issued) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        published = issued;
+        if (lane == 0) publish(&landed[pw], published);
+      }
+    };
+    int seen = 0;  // a lower bound of every consumer's count (they only grow)
+    while (pc.left > 0) {
+      const int need = issued - C::NS + 1;  // the slot's previous item must be done
+      // While the slot is busy, publish the oldest unpublished item one at a
+      // time (the consumers may be waiting for it), else sleep.
+      for (int n = 0; seen < need && n < kSpinLimit; ++n) {
+        if ((seen = consumed_min()) >= need) break;
+        if (published < issued) {
+          wait_items<C::PER, C::NS - 1>(issued - published - 1);
+          ++published;
+          if (lane == 0) publish(&landed[pw], published);
+        } else {
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      issue(pc, issued % C::NS);
       advance(pc);
+      ++issued;
+      if (issued - published > C::DEPTH) {  // keep DEPTH items in flight, publish the rest
+        vm_wait_imm<C::PER, C::DEPTH>();
+        published = issued - C::DEPTH;
+        if (lane == 0) publish(&landed[pw], published);
+      }
     }
+    publish_all();
+    return;
   }
+  int seg = 0, have = 0;  // have: a lower bound of the landed count
+  auto wait_landed = [&](int v) {
+    if (have < v) spin_until(([&] { return (have = landed_min()) >= v; }));
+  };
   for (int i = 0; cc.left > 0;) {
-    // The next group: a job's query items, or up to two K/V steps of a job.
+    // The next group: a job's query items (read by every consumer wave), or
+    // one K/V step per parity.
     const bool qgrp = cc.phase < cc.nq;
     const int gsz = qgrp ? cc.nq : ((cc.left >= 2 && cc.step + 1 < cc.n) ? 2 : 1);
-    if (producer) wait_items<C::PER, C::NS - 1>(issued - (i + gsz));
-    __syncthreads();  // the group is in LDS; slots of earlier items are free
-    if (producer) {
-      while (pc.left > 0 && issued < i + C::NS) {
-        issue(pc, issued % C::NS);
-        advance(pc);
-        ++issued;
-      }
-    } else if (qgrp) {
-      if (tid == 0 && cc.step == 0)  // this workgroup starts the job
+    if (qgrp) {
+      wait_landed(i + gsz);
+      if (lane == 0 && hb == 0 && par == 0 && cc.step == 0)  // this workgroup starts the job
         a.job_seg[2 * ((int64_t)cc.b * jpb + cc.jb)] = w_id;
       m_run = kNegInf;
       l_run = 0.0f;
@@ -520,12 +590,16 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
           qf[ds] = __builtin_bit_cast(bf16x8, raw);
         }
       }
-    } else if (par < gsz && hb * 32 < cc.rows) {
-      kv_group(One{}, i + par, cc.step + par, cc.Lb);
-    }
-    if (!qgrp) {
+      if (lane == 0) publish(&consumed[wave], i + gsz);
+    } else {
+      const bool mine = par < gsz && hb * 32 < cc.rows;
+      if (mine) {
+        wait_landed(i + par + 1);
+        kv_group(One{}, i + par, cc.step + par, cc.Lb);
+      }
+      if (lane == 0) publish(&consumed[wave], i + gsz);
       const bool job_end = cc.step + gsz == cc.n;
-      if (job_end || cc.left == gsz) finish_segment(cc, job_end);
+      if (job_end || cc.left == gsz) finish_segment(cc, job_end, seg++);
     }
     for (int t = 0; t < gsz; ++t) advance(cc);
     i += gsz;
