@@ -35,3 +35,4 @@ from .attention import (  # noqa: F401
     decode_split,
     kv_head_of,
 )
+from .kvcache import cache_rows, decode_kvcache, kvcache_append  # noqa: F401
