@@ -16,7 +16,8 @@ Besides the headline line the JSON carries:
   kernels       per-kernel times and rates from the same events;
   extra         the other workloads: split-K decode over a KV cache (HBM
                 GB/s, 8 rotating cache copies so the 256 MB last-level cache
-                cannot hold the working set), long-context local attention
+                cannot hold the working set; contiguous and in 256-row pages
+                through a random block table), long-context local attention
                 with ALiBi / softcap, the packed-document block-sparse mask
                 (device mask build and forward);
   cpu_baseline  the fp64 CPU oracle timed on this host on one full step of the
@@ -236,6 +237,35 @@ def timed(torch, np, fn, reps, warm=2):
     return float(np.median(ts)), float(np.min(ts))
 
 
+def graph_timed(torch, np, make_calls, reps=10):
+    """GPU time per call of a short call sequence: the calls (built for the
+    given stream) are captured once into a HIP graph and the graph is
+    replayed; host launch overhead is not part of the figure.  Returns
+    (ms per call, the eager and replayed outputs of the last call agree)."""
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        calls, out = make_calls(ctypes.c_void_p(st.cuda_stream))
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, eager))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(calls)), same
+
+
 def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
     ex = {}
     # decode: B=32, Hq=128, Hkv=1, D=128, cache lengths in [1024, 8192]
@@ -265,14 +295,78 @@ def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
         it[0] += 1
 
     med, mn = timed(torch, np, dec, 40)
+
+    def make_dec(st):
+        cs = []
+        for qq, kk, vv in copies:
+            p = b._params(qq, kk, Dd, w["scale"], False, (-1, -1), None, 0.0, None)
+            cs.append(Prepared(lib.attn_decode, (ctypes.byref(p), b._tensor(qq), b._tensor(kk),
+                                                 b._tensor(vv), b._ptr(lens), 0, b._tensor(o),
+                                                 b._ptr(lse), b._ptr(ws), ws.numel(), st)))
+            cs[-1].keep = p
+        return cs, o
+
+    gms, gsame = graph_timed(torch, np, make_dec)
     algo_bytes = total * Dd * 2 * 2 + 2 * Bd * Hqd * Dd * 2 + Bd * Hqd * 4
     ex["decode_mqa_b32_h128"] = {
-        "ms": round(med, 5), "ms_min": round(mn, 5),
-        "hbm_gbs": round(algo_bytes / (med * 1e-3) / 1e9, 1),
-        "frac_of_hbm_peak": round(algo_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "tflops": round(4.0 * Hqd * Dd * total / (med * 1e-3) / 1e12, 2),
+        "ms": round(gms, 5), "graph_replay_matches_eager": gsame,
+        "ms_eager_launches": round(med, 5), "ms_eager_min": round(mn, 5),
+        "hbm_gbs": round(algo_bytes / (gms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(algo_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "tflops": round(4.0 * Hqd * Dd * total / (gms * 1e-3) / 1e12, 2),
         "algorithmic_bytes": algo_bytes}
-    del copies, o, ws
+    del copies
+
+    # the same decode over a paged cache (256-row pages, seeded random block table)
+    inputs.to_pages(w, 256)
+    table = torch.from_numpy(w["block_table"]).to(dev)
+    pcopies = [(to_dev(w["q"]), to_dev(w["k_pages"]), to_dev(w["v_pages"])) for _ in range(8)]
+    pcalls = []
+    for qq, kk, vv in pcopies:
+        p = b._params(qq, kk, Dd, w["scale"], False, (-1, -1), None, 0.0, None)
+        p.Sk = w["block_table"].shape[1] * 256
+        kv = b.attn_kvcache()
+        kv.block_table = table.data_ptr()
+        kv.max_blocks = w["block_table"].shape[1]
+        kv.page_size = 256
+        kv.num_pages = kk.shape[0]
+        pcalls.append(Prepared(lib.attn_decode_kvcache,
+                               (ctypes.byref(p), b._tensor(qq), b._tensor(kk), b._tensor(vv),
+                                b._ptr(lens), ctypes.byref(kv), 0, b._tensor(o), b._ptr(lse),
+                                b._ptr(ws), ws.numel(), stream)))
+        pcalls[-1].keep = (p, kv)
+    it[0] = 0
+
+    def decp():
+        pcalls[it[0] % 8]()
+        it[0] += 1
+
+    med, mn = timed(torch, np, decp, 40)
+
+    def make_decp(st):
+        cs = []
+        for qq, kk, vv in pcopies:
+            p = b._params(qq, kk, Dd, w["scale"], False, (-1, -1), None, 0.0, None)
+            p.Sk = w["block_table"].shape[1] * 256
+            kv = b.attn_kvcache()
+            kv.block_table = table.data_ptr()
+            kv.max_blocks = w["block_table"].shape[1]
+            kv.page_size = 256
+            kv.num_pages = kk.shape[0]
+            cs.append(Prepared(lib.attn_decode_kvcache,
+                               (ctypes.byref(p), b._tensor(qq), b._tensor(kk), b._tensor(vv),
+                                b._ptr(lens), ctypes.byref(kv), 0, b._tensor(o), b._ptr(lse),
+                                b._ptr(ws), ws.numel(), st)))
+            cs[-1].keep = (p, kv)
+        return cs, o
+
+    gms, gsame = graph_timed(torch, np, make_decp)
+    ex["decode_mqa_b32_h128_paged256"] = {
+        "ms": round(gms, 5), "graph_replay_matches_eager": gsame,
+        "ms_eager_launches": round(med, 5), "ms_eager_min": round(mn, 5),
+        "hbm_gbs": round(algo_bytes / (gms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(algo_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del pcopies, o, ws
 
     # long-context local attention: S=16384, causal + window (4096, 0)
     w = inputs.long_local()

@@ -98,6 +98,20 @@ _lib.attn_decode.restype = ctypes.c_int
 _lib.attn_decode.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor,
                              ctypes.c_void_p, ctypes.c_int32, attn_tensor, ctypes.c_void_p,
                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+
+class attn_kvcache(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("cache_batch_idx", ctypes.c_void_p), ("cache_batch", ctypes.c_int32),
+                ("k_new", attn_tensor), ("v_new", attn_tensor), ("s_new", ctypes.c_int32)]
+
+
+_lib.attn_decode_kvcache.restype = ctypes.c_int
+_lib.attn_decode_kvcache.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor,
+                                     ctypes.c_void_p, _P(attn_kvcache), ctypes.c_int32,
+                                     attn_tensor, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p]
 _lib.attn_decode_workspace_size.restype = ctypes.c_size_t
 _lib.attn_decode_workspace_size.argtypes = [_P(attn_params), ctypes.c_int32]
 _lib.attn_block_mask_bytes.restype = ctypes.c_size_t
@@ -110,7 +124,8 @@ _lib.block_mask_build.argtypes = [_P(attn_mask_desc), ctypes.c_int32, ctypes.c_i
 
 EXPORTED = ["attn_status_string", "attn_last_error", "attn_fwd", "attn_fwd_tile_shape",
             "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_size", "attn_decode",
-            "attn_decode_workspace_size", "attn_block_mask_bytes", "block_mask_build"]
+            "attn_decode_kvcache", "attn_decode_workspace_size", "attn_block_mask_bytes",
+            "block_mask_build"]
 
 
 def library():
@@ -279,11 +294,37 @@ def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softma
 
 
 def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=0.0,
-                num_splits=0, out=None, lse=None, workspace=None):
-    """Decode over a KV cache.  q [B, 1, Hq, D]; caches [B, Smax, Hkv, D];
-    cache_seqlens int32 [B] on the device.  Returns (out, lse [B, Hq, 1])."""
+                num_splits=0, out=None, lse=None, workspace=None, block_table=None,
+                cache_batch_idx=None, k_new=None, v_new=None):
+    """Decode over a KV cache.  q [B, 1, Hq, D]; caches [B, Smax, Hkv, D]
+    (paged: [num_pages, page_size, Hkv, D] with block_table int32
+    [B, max_blocks]); cache_seqlens int32 [B] on the device; optional
+    cache_batch_idx int32 [B] (contiguous caches) and k_new / v_new
+    [B, s_new, Hkv, D] appended in place at rows [L_b, L_b + s_new).
+    Returns (out, lse [B, Hq, 1])."""
     B, Sq, Hq, D = q.shape
     p = _params(q, k_cache, D, softmax_scale, False, (-1, -1), None, softcap, None)
+    kv = None
+    if block_table is not None or cache_batch_idx is not None or k_new is not None:
+        kv = attn_kvcache()
+        if block_table is not None:
+            if block_table.dtype != torch.int32 or block_table.dim() != 2:
+                raise ValueError("block_table must be a 2-d int32 tensor")
+            if not block_table.is_contiguous():
+                raise ValueError("block_table must be contiguous")
+            kv.block_table = block_table.data_ptr()
+            kv.max_blocks = block_table.shape[1]
+            kv.page_size = k_cache.shape[1]
+            kv.num_pages = k_cache.shape[0]
+            p.Sk = block_table.shape[1] * k_cache.shape[1]
+        if cache_batch_idx is not None:
+            if cache_batch_idx.dtype != torch.int32:
+                raise ValueError("cache_batch_idx must be int32")
+            kv.cache_batch_idx = cache_batch_idx.data_ptr()
+            kv.cache_batch = k_cache.shape[0]
+        if k_new is not None:
+            kv.k_new, kv.v_new = _tensor(k_new), _tensor(v_new)
+            kv.s_new = k_new.shape[1]
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -293,9 +334,15 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
     need = _lib.attn_decode_workspace_size(ctypes.byref(p), int(num_splits))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(_lib.attn_decode(ctypes.byref(p), _tensor(q), _tensor(k_cache), _tensor(v_cache),
-                            _ptr(cache_seqlens), int(num_splits), _tensor(out), _ptr(lse),
-                            _ptr(workspace), workspace.numel(), _stream()))
+    if kv is None:
+        _check(_lib.attn_decode(ctypes.byref(p), _tensor(q), _tensor(k_cache), _tensor(v_cache),
+                                _ptr(cache_seqlens), int(num_splits), _tensor(out), _ptr(lse),
+                                _ptr(workspace), workspace.numel(), _stream()))
+    else:
+        _check(_lib.attn_decode_kvcache(ctypes.byref(p), _tensor(q), _tensor(k_cache),
+                                        _tensor(v_cache), _ptr(cache_seqlens), ctypes.byref(kv),
+                                        int(num_splits), _tensor(out), _ptr(lse), _ptr(workspace),
+                                        workspace.numel(), _stream()))
     return out, lse
 
 

@@ -315,10 +315,10 @@ size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits) {
   return attn::decode_workspace(p->B, p->Hq, p->Hkv, p->D, attn::decode_parts(num_splits)).bytes;
 }
 
-attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache,
-                        attn_tensor v_cache, const int32_t* cache_seqlens, int32_t num_splits,
-                        attn_tensor o, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor k_cache,
+                               attn_tensor v_cache, const int32_t* cache_seqlens,
+                               const attn_kvcache* kv, int32_t num_splits, attn_tensor o, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   Common cm;
   attn_status st = check_params(p, &cm);
@@ -329,9 +329,35 @@ attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports scale and softcap only");
   const int32_t dt = q.dtype;
   if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports bf16 only");
+  const bool paged = kv != nullptr && kv->block_table != nullptr;
+  const bool remap = kv != nullptr && kv->cache_batch_idx != nullptr;
+  const bool append = kv != nullptr && kv->k_new.data != nullptr;
+  if (kv != nullptr && (kv->k_new.data == nullptr) != (kv->v_new.data == nullptr))
+    return fail(ATTN_ERR_INVALID_ARG, "k_new and v_new must be given together");
+  if (paged && remap)
+    return fail(ATTN_ERR_UNSUPPORTED, "cache_batch_idx is for contiguous caches (not with block_table)");
+  if (paged) {
+    if (kv->page_size <= 0 || kv->page_size % 32 != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "page_size must be a positive multiple of 32 (got %d)", kv->page_size);
+    if (kv->max_blocks <= 0 || kv->num_pages <= 0)
+      return fail(ATTN_ERR_INVALID_ARG, "max_blocks and num_pages must be positive");
+    if ((int64_t)kv->max_blocks * kv->page_size != p->Sk)
+      return fail(ATTN_ERR_INVALID_ARG, "paged cache: Sk (%d) must equal max_blocks * page_size (%lld)",
+                  p->Sk, (long long)kv->max_blocks * kv->page_size);
+  }
+  if (remap && kv->cache_batch <= 0)
+    return fail(ATTN_ERR_INVALID_ARG, "cache_batch must be positive with cache_batch_idx");
+  if (append && (kv->s_new <= 0 || kv->s_new > p->Sk))
+    return fail(ATTN_ERR_INVALID_ARG, "s_new must be in [1, Sk] (got %d)", kv->s_new);
   if ((st = check_tensor("q", q, dt, p->B, 1, p->Hq, true)) != ATTN_OK) return st;
-  if ((st = check_tensor("k_cache", k_cache, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
-  if ((st = check_tensor("v_cache", v_cache, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
+  const int64_t cache_rows0 = paged ? kv->num_pages : (remap ? kv->cache_batch : p->B);
+  const int64_t cache_rows1 = paged ? kv->page_size : p->Sk;
+  if ((st = check_tensor("k_cache", k_cache, dt, cache_rows0, cache_rows1, p->Hkv, true)) != ATTN_OK) return st;
+  if ((st = check_tensor("v_cache", v_cache, dt, cache_rows0, cache_rows1, p->Hkv, true)) != ATTN_OK) return st;
+  if (append) {
+    if ((st = check_tensor("k_new", kv->k_new, dt, p->B, kv->s_new, p->Hkv, true)) != ATTN_OK) return st;
+    if ((st = check_tensor("v_new", kv->v_new, dt, p->B, kv->s_new, p->Hkv, true)) != ATTN_OK) return st;
+  }
   if ((st = check_tensor("o", o, dt, p->B, 1, p->Hq, true)) != ATTN_OK) return st;
   if (p->B > 0 && (cache_seqlens == nullptr || lse == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "cache_seqlens and lse must not be NULL");
@@ -355,6 +381,25 @@ attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.D = p->D; a.Smax = p->Sk;
   a.scale = cm.scale;
   a.softcap = p->softcap;
+  if (paged) {
+    a.block_table = kv->block_table;
+    a.max_blocks = kv->max_blocks;
+    a.page_size = kv->page_size;
+    a.num_pages = kv->num_pages;
+    a.k_pg = k_cache.stride[0];
+    a.v_pg = v_cache.stride[0];
+  }
+  if (remap) {
+    a.batch_idx = kv->cache_batch_idx;
+    a.cache_batch = kv->cache_batch;
+  }
+  if (append) {
+    a.len_add = kv->s_new;
+    a.k_new = kv->k_new.data;
+    a.v_new = kv->v_new.data;
+    strides3(kv->k_new, &a.kn_sb, &a.kn_ss, &a.kn_sh);
+    strides3(kv->v_new, &a.vn_sb, &a.vn_ss, &a.vn_sh);
+  }
   a.parts = attn::decode_parts(num_splits);
   a.nhg = attn::decode_head_groups(p->Hq, p->Hkv);
   const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->D, a.parts);
@@ -363,6 +408,22 @@ attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache
   a.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
   a.job_seg = reinterpret_cast<int32_t*>(wsb + wl.seg_off);
   return hip_status(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "attn_decode launch");
+}
+
+attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache,
+                        attn_tensor v_cache, const int32_t* cache_seqlens, int32_t num_splits,
+                        attn_tensor o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, cache_seqlens, nullptr, num_splits, o, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+attn_status attn_decode_kvcache(const attn_params* p, attn_tensor q, attn_tensor k_cache,
+                                attn_tensor v_cache, const int32_t* cache_seqlens,
+                                const attn_kvcache* kv, int32_t num_splits, attn_tensor o,
+                                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, cache_seqlens, kv, num_splits, o, lse, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t attn_block_mask_bytes(int32_t B, int32_t Sq, int32_t Sk, int32_t block_m, int32_t block_n) {

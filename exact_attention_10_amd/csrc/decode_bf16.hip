@@ -81,6 +81,21 @@ __device__ __forceinline__ void spin_until_ge(const int* p, int v) {
 
 __device__ __forceinline__ int clamp_len(int L, int smax) { return L < 0 ? 0 : (L > smax ? smax : L); }
 
+// Keys sequence b attends to: its cache length (clamped so that the appended
+// rows fit the capacity) plus the appended rows.
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  return clamp_len(a.seqlens[b], a.Smax - a.len_add) + a.len_add;
+}
+
+// One int32 through the scalar cache (p must be wave-uniform).  Used by the
+// producer waves for page and batch-row lookups: a vector load would make
+// the compiler wait for all of their outstanding copies.
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
 // Wait until at most PER * k copies of this lane are outstanding.
 template <int PER, int K>
 __device__ __forceinline__ void vm_wait_imm() {
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   // ---- this workgroup's step range [lo, hi) ----
   long long S, lo, hi;
   if (a.B <= C::NT) {  // one pass: every thread keeps its sequence's length
-    const int Lt = tid < a.B ? clamp_len(a.seqlens[tid], a.Smax) : 0;
+    const int Lt = tid < a.B ? seq_len(a, tid) : 0;
     const int n = (Lt + C::BN - 1) / C::BN;
     const long long pre = block_excl_scan<C::NWT>((long long)n * jpb, red, &S);
     const int Pe = S < P ? (int)S : P;
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     S = 0;
     for (int base = 0; base < a.B; base += C::NT) {
       const int b = base + tid;
-      const int n = b < a.B ? (clamp_len(a.seqlens[b], a.Smax) + C::BN - 1) / C::BN : 0;
+      const int n = b < a.B ? (seq_len(a, b) + C::BN - 1) / C::BN : 0;
       S += block_sum<C::NWT>(n, red);
     }
     S *= jpb;
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     long long carry = 0;
     for (int base = 0; base < a.B; base += C::NT) {
       const int b = base + tid;
-      const int n = b < a.B ? (clamp_len(a.seqlens[b], a.Smax) + C::BN - 1) / C::BN : 0;
+      const int n = b < a.B ? (seq_len(a, b) + C::BN - 1) / C::BN : 0;
       long long tot;
       const long long pre = carry + block_excl_scan<C::NWT>((long long)n * jpb, red, &tot);
       if (n > 0 && pre <= lo && lo < pre + (long long)n * jpb) {
@@ -225,7 +240,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     __syncthreads();
     const int b0 = (int)sh_b0;
     for (int i = tid; i < C::WIN; i += C::NT)
-      win_len[i] = b0 + i < a.B ? clamp_len(a.seqlens[b0 + i], a.Smax) : 0;
+      win_len[i] = b0 + i < a.B ? seq_len(a, b0 + i) : 0;
   }
   if (tid < C::NWP) landed[tid] = 0;
   if (tid < C::NWC) consumed[tid] = 0;
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   auto consumed_min = [&]() { return counters_min(consumed, std::integral_constant<int, C::NWC>{}); };
 
   auto len_of = [&](int b) -> int {
-    return b - b0 < C::WIN ? win_len[b - b0] : clamp_len(a.seqlens[b], a.Smax);
+    return b - b0 < C::WIN ? win_len[b - b0] : seq_len(a, b);
   };
   auto set_job = [&](Cursor& cu) {
     cu.g_kv = cu.jb / a.nhg;
@@ -295,6 +310,8 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   // chunk l / RG.
   const int pw = producer ? wave - C::NWC : 0;
 
+  int pg_b = -1, pg_blk = -1, pg_page = 0;  // last page lookup (producers)
+  int cb_b = -1, cb_row = 0;                // last batch-row lookup (producers)
   auto issue = [&](const Cursor& pc, int slot) {
     // (Lane constants are recomputed here so that they do not occupy
     // registers in the consumer waves.)
@@ -312,10 +329,27 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       }
     } else {
       const int row0 = pc.step * C::BN;
-      const char* kb = static_cast<const char*>(a.k) +
-                       ((int64_t)pc.b * a.k_sb + (int64_t)pc.g_kv * a.k_sh + (int64_t)row0 * a.k_ss) * 2;
-      const char* vb = static_cast<const char*>(a.v) +
-                       ((int64_t)pc.b * a.v_sb + (int64_t)pc.g_kv * a.v_sh + (int64_t)row0 * a.v_ss) * 2;
+      int64_t koff, voff;  // element offsets of the item's first row
+      if (a.block_table != nullptr) {  // an item never straddles pages (page_size % 32 == 0)
+        const int blk = row0 / a.page_size;
+        if (pc.b != pg_b || blk != pg_blk) {
+          pg_b = pc.b;
+          pg_blk = blk;
+          pg_page = clamp_len(sload_i32(a.block_table + (int64_t)pc.b * a.max_blocks + blk), a.num_pages - 1);
+        }
+        const int prow = row0 - blk * a.page_size;
+        koff = (int64_t)pg_page * a.k_pg + (int64_t)prow * a.k_ss;
+        voff = (int64_t)pg_page * a.v_pg + (int64_t)prow * a.v_ss;
+      } else {
+        if (pc.b != cb_b) {
+          cb_b = pc.b;
+          cb_row = a.batch_idx != nullptr ? clamp_len(sload_i32(a.batch_idx + pc.b), a.cache_batch - 1) : pc.b;
+        }
+        koff = (int64_t)cb_row * a.k_sb + (int64_t)row0 * a.k_ss;
+        voff = (int64_t)cb_row * a.v_sb + (int64_t)row0 * a.v_ss;
+      }
+      const char* kb = static_cast<const char*>(a.k) + (koff + (int64_t)pc.g_kv * a.k_sh) * 2;
+      const char* vb = static_cast<const char*>(a.v) + (voff + (int64_t)pc.g_kv * a.v_sh) * 2;
       if (row0 + C::BN <= pc.Lb) {
         const int64_t koff = ((int64_t)lrow * a.k_ss + cp_chunk * 8) * 2;  // bytes, from a group's first row
         const int64_t voff = ((int64_t)lrow * a.v_ss + cp_chunk * 8) * 2;
@@ -625,7 +659,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (r >= rows) return;
   const int d4 = threadIdx.x % TPH;
   const int h = g_kv * G + hg * ROWS + r;
-  const int Lb = clamp_len(a.seqlens[b], a.Smax);
+  const int Lb = seq_len(a, b);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float m = kNegInf, tot = 0.0f;
   if (Lb > 0) {
@@ -675,8 +709,48 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (d4 == 0) a.lse[(int64_t)b * a.Hq + h] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
 }
 
+// In-place append: rows [L_b, L_b + len_add) of sequence b's cache (paged or
+// contiguous) receive k_new / v_new.  One thread per 16-byte chunk.
+template <int D>
+__global__ __launch_bounds__(256) void kvcache_append_kernel(DecodeArgs a) {
+  constexpr int CH = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.len_add * a.Hkv * CH;
+  if (idx >= total) return;
+  const int ch = (int)(idx % CH);
+  int64_t rest = idx / CH;
+  const int g = (int)(rest % a.Hkv);
+  rest /= a.Hkv;
+  const int t = (int)(rest % a.len_add);
+  const int b = (int)(rest / a.len_add);
+  const int r = clamp_len(a.seqlens[b], a.Smax - a.len_add) + t;
+  int64_t koff, voff;
+  if (a.block_table != nullptr) {
+    const int blk = r / a.page_size;
+    const int page = clamp_len(a.block_table[(int64_t)b * a.max_blocks + blk], a.num_pages - 1);
+    koff = (int64_t)page * a.k_pg + (int64_t)(r - blk * a.page_size) * a.k_ss;
+    voff = (int64_t)page * a.v_pg + (int64_t)(r - blk * a.page_size) * a.v_ss;
+  } else {
+    const int row = a.batch_idx != nullptr ? clamp_len(a.batch_idx[b], a.cache_batch - 1) : b;
+    koff = (int64_t)row * a.k_sb + (int64_t)r * a.k_ss;
+    voff = (int64_t)row * a.v_sb + (int64_t)r * a.v_ss;
+  }
+  bf16_t* kd = static_cast<bf16_t*>(const_cast<void*>(a.k)) + koff + (int64_t)g * a.k_sh + 8 * ch;
+  bf16_t* vd = static_cast<bf16_t*>(const_cast<void*>(a.v)) + voff + (int64_t)g * a.v_sh + 8 * ch;
+  const bf16_t* ks = static_cast<const bf16_t*>(a.k_new) + b * a.kn_sb + (int64_t)t * a.kn_ss + g * a.kn_sh + 8 * ch;
+  const bf16_t* vs = static_cast<const bf16_t*>(a.v_new) + b * a.vn_sb + (int64_t)t * a.vn_ss + g * a.vn_sh + 8 * ch;
+  *reinterpret_cast<uint4*>(kd) = *reinterpret_cast<const uint4*>(ks);
+  *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
+}
+
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+  if (a.len_add > 0) {
+    const int64_t total = (int64_t)a.B * a.len_add * a.Hkv * (D / 8);
+    hipLaunchKernelGGL(kvcache_append_kernel<D>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 block(DecCfg<D>::NT);
   if (a.softcap > 0.0f) hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(a.parts), block, 0, s, a);
   else hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(a.parts), block, 0, s, a);

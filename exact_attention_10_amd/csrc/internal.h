@@ -99,6 +99,19 @@ struct DecodeArgs {
   float* part_o;             // workspace [parts + jobs][kDecodeRows][D]
   float* part_lse;           // workspace [parts + jobs][kDecodeRows]
   int32_t* job_seg;          // workspace [jobs][2]: first and last workgroup of each job
+  // KV-cache addressing.  Contiguous: sequence b uses batch row batch_idx[b]
+  // (b when null) of k/v.  Paged (block_table != null): row r of sequence b is
+  // row r % page_size of page block_table[b * max_blocks + r / page_size],
+  // k_pg / v_pg being the page strides.  Smax is the per-sequence capacity.
+  const int32_t* batch_idx;
+  int cache_batch;           // batch rows of a contiguous cache (batch_idx range)
+  const int32_t* block_table;
+  int max_blocks, page_size, num_pages;
+  int64_t k_pg, v_pg;
+  // In-place append of len_add new rows per sequence at [L_b, L_b + len_add).
+  int len_add;
+  const void* k_new; const void* v_new;
+  int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;
 };
 constexpr int kDecodeRows = 128;  // query heads per decode job
 // Number of workgroups: num_splits when > 0, else the device's compute units.

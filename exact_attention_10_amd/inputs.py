@@ -146,6 +146,35 @@ def decode_mqa(seed=5, B=32, Hq=128, Smax=8192, D=128, lmin=1024, lmax=8192):
     return w
 
 
+def to_pages(w, page_size, seed=17, spare_pages=5):
+    """The same cache laid out as pages: every sequence's rows are scattered
+    over a seeded random permutation of [num_pages, page_size, Hkv, D] pages
+    (a few spare pages hold random junk).  Adds k_pages, v_pages and the
+    int32 block_table [B, Smax / page_size] to a decode workload."""
+    rng = np.random.default_rng(seed)
+    k, v = w["k"], w["v"]
+    B, Smax = k.shape[:2]
+    assert Smax % page_size == 0
+    nblk = Smax // page_size
+    num_pages = B * nblk + spare_pages
+    table = rng.permutation(num_pages)[: B * nblk].reshape(B, nblk).astype(np.int32)
+    kp = _normals(rng, (num_pages, page_size) + k.shape[2:], "bf16")
+    vp = _normals(rng, (num_pages, page_size) + v.shape[2:], "bf16")
+    for b in range(B):
+        kp[table[b]] = k[b].reshape((nblk, page_size) + k.shape[2:])
+        vp[table[b]] = v[b].reshape((nblk, page_size) + v.shape[2:])
+    w.update(k_pages=kp, v_pages=vp, block_table=table, page_size=page_size)
+    return w
+
+
+def new_tokens(w, s_new, seed=19):
+    """Seeded new keys / values [B, s_new, Hkv, D] for an in-place append."""
+    rng = np.random.default_rng(seed)
+    shape = (w["k"].shape[0], s_new) + w["k"].shape[2:]
+    w.update(k_new=_normals(rng, shape, "bf16"), v_new=_normals(rng, shape, "bf16"))
+    return w
+
+
 def as_f64(x, dtype):
     """The values a consumer of stored inputs sees, widened to fp64."""
     if dtype == "bf16":

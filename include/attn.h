@@ -244,6 +244,44 @@ attn_status attn_decode(const attn_params* p, attn_tensor q,
 size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits);
 
 /* ---------------------------------------------------------------------
+ * Decode over a paged and/or batch-indexed KV cache with in-place append
+ * ([FA] flash_attn_with_kvcache: "k_cache, v_cache: cached keys/values,
+ * updated inplace", arguments k, v, cache_batch_idx, block_table).
+ *   block_table : device int32 [B, max_blocks] or NULL.  When set, k_cache and
+ *       v_cache are [num_pages, page_size, Hkv, D] and row r of sequence b is
+ *       row r % page_size of page block_table[b, r / page_size]; page_size
+ *       is a positive multiple of 32 and p->Sk must equal
+ *       max_blocks * page_size (the per-sequence capacity).  Entries outside
+ *       [0, num_pages) are clamped to that range on the device.
+ *   cache_batch_idx : device int32 [B] or NULL (contiguous caches only):
+ *       sequence b uses batch row cache_batch_idx[b] of k_cache / v_cache,
+ *       which then have cache_batch rows ([cache_batch, Sk, Hkv, D]); values
+ *       are clamped to [0, cache_batch).
+ *   k_new, v_new : [B, s_new, Hkv, D] bf16 (data NULL = no append).  Before
+ *       attending, rows [L_b, L_b + s_new) of each sequence's cache receive
+ *       them (L_b = cache_seqlens[b], clamped to [0, Sk - s_new]) and the
+ *       query then attends to L_b + s_new rows.  cache_seqlens is read, not
+ *       advanced.  The caches are written in place (stream-ordered).
+ * Other arguments, outputs, workspace and errors as attn_decode (which is
+ * this call with a NULL kv).  Errors: INVALID_ARG for a page_size that is
+ * not a positive multiple of 32, a capacity mismatch, k_new without v_new,
+ * s_new outside [1, Sk]; UNSUPPORTED for block_table with cache_batch_idx. */
+typedef struct {
+  const int32_t* block_table;
+  int32_t max_blocks;
+  int32_t page_size;
+  int32_t num_pages;
+  const int32_t* cache_batch_idx;
+  int32_t cache_batch;
+  attn_tensor k_new, v_new;
+  int32_t s_new;
+} attn_kvcache;
+attn_status attn_decode_kvcache(const attn_params* p, attn_tensor q, attn_tensor k_cache,
+                                attn_tensor v_cache, const int32_t* cache_seqlens,
+                                const attn_kvcache* kv, int32_t num_splits, attn_tensor o,
+                                float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * Block-mask construction on the device ([GYM] create_block_mask with
  * BLOCK_SIZE; [FX4] block-sparse masks skip tiles with nothing to compute).
  * Classifies every tile by evaluating the predicate of `m` on every in-bounds
