@@ -425,6 +425,29 @@ def test_bwd_gqa_equals_group_sum_of_mha():
     np.testing.assert_allclose(dv, dv2.reshape(1, 9, 2, 4, 3).sum(3), atol=1e-14)
 
 
+def test_bwd_documents_are_independent():
+    """[P16] With a document mask (causal inside each document, [GYM] packed
+    sequences), the gradients of a packed sequence are the gradients of each
+    document run on its own: the slices are concatenated and compared."""
+    rng = np.random.default_rng(12)
+    lens = inputs.doc_lengths(rng, 160, 10, 60)
+    doc = inputs.doc_ids(lens)[None]
+    S, Hq, Hkv, D = 160, 4, 2, 8
+    q, k, v, do = (rng.standard_normal(s) for s in
+                   [(1, S, Hq, D), (1, S, Hkv, D), (1, S, Hkv, D), (1, S, Hq, D)])
+    kw = dict(scale=0.6, softcap=2.5)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal=True, doc_q=doc, doc_k=doc, **kw)
+    s0 = 0
+    for n in lens:
+        sl = slice(s0, s0 + n)
+        eq, ek, ev = oracle.attention_bwd(q[:, sl], k[:, sl], v[:, sl], do[:, sl], causal=True, **kw)
+        np.testing.assert_allclose(dq[:, sl], eq, atol=1e-13)
+        np.testing.assert_allclose(dk[:, sl], ek, atol=1e-13)
+        np.testing.assert_allclose(dv[:, sl], ev, atol=1e-13)
+        s0 += n
+    assert s0 == S and len(lens) > 2
+
+
 def test_bwd_delta_identity():
     """Delta_i = sum_j P_ij dP_ij equals <dO_i, O_i> (the form a kernel
     uses); checked through dQ of a case whose O is known."""
