@@ -265,10 +265,10 @@ def attn_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), alibi_s
 
 def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, window=(-1, -1),
              alibi_slopes=None, softcap=0.0, deterministic=True, dq=None, dk=None, dv=None,
-             workspace=None):
+             workspace=None, block_mask=None):
     """Backward attention from the saved LSE.  Returns (dq, dk, dv)."""
     D = q.shape[3]
-    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, None)
+    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -283,11 +283,11 @@ def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, window=(
 
 
 def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softmax_scale=None,
-                   causal=False, window=(-1, -1), alibi_slopes=None, softcap=0.0):
+                   causal=False, window=(-1, -1), alibi_slopes=None, softcap=0.0, block_mask=None):
     """Enqueue one stage (0 Delta, 1 dK/dV, 2 group sum, 3 dQ) of attn_bwd;
     stages 0..3 in order with one workspace equal attn_bwd."""
     D = q.shape[3]
-    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, None)
+    p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask)
     _check(_lib.attn_bwd_stage(ctypes.byref(p), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
                                _tensor(dout), _ptr(lse), _tensor(dq), _tensor(dk), _tensor(dv), 1,
                                _ptr(workspace), workspace.numel(), int(stage), _stream()))

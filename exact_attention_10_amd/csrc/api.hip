@@ -244,8 +244,16 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
   if ((st = check_tensor("dk", dk, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
   if ((st = check_tensor("dv", dv, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
   if (lse == nullptr && p->B * p->Sq > 0) return fail(ATTN_ERR_INVALID_ARG, "lse is NULL");
-  if (p->block_mask != nullptr)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd does not take block masks");
+  if ((st = check_block_mask(p, dt)) != ATTN_OK) return st;
+  if (p->block_mask != nullptr) {
+    const attn_block_mask* bm = p->block_mask;
+    if (bm->block_n % 128 != 0)
+      return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd takes block masks with block_n a multiple of 128 (got %d)",
+                  bm->block_n);
+    if (bm->q_num_full == nullptr || bm->q_idx_full == nullptr || bm->q_num_partial == nullptr ||
+        bm->q_idx_partial == nullptr)
+      return fail(ATTN_ERR_INVALID_ARG, "block mask query lists are NULL (attn_bwd needs them)");
+  }
   if (deterministic != 1)
     return fail(ATTN_ERR_UNSUPPORTED, "only the deterministic backward (deterministic=1) is implemented");
   const size_t need = attn_bwd_workspace_size(p);
@@ -272,6 +280,20 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
   a.alibi_sb = p->alibi_batch_stride;
   a.softcap = p->softcap;
   a.mask = mask_from(p);
+  if (p->block_mask != nullptr) {
+    const attn_block_mask* bm = p->block_mask;
+    a.tiles.kv_num_full = bm->kv_num_full;
+    a.tiles.kv_idx_full = bm->kv_idx_full;
+    a.tiles.kv_num_partial = bm->kv_num_partial;
+    a.tiles.kv_idx_partial = bm->kv_idx_partial;
+    a.tiles.q_num_full = bm->q_num_full;
+    a.tiles.q_idx_full = bm->q_idx_full;
+    a.tiles.q_num_partial = bm->q_num_partial;
+    a.tiles.q_idx_partial = bm->q_idx_partial;
+    a.tiles.nQ = bm->nQ;
+    a.tiles.nK = bm->nK;
+    a.tiles.block_n = bm->block_n;
+  }
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   a.delta = static_cast<float*>(workspace);
   const size_t rows_bytes = up((size_t)p->B * p->Hq * p->Sq * sizeof(float));

@@ -159,7 +159,8 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
                                           const float* dl_t, const bf16x8 (&kf)[D / 16],
                                           const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
                                           f32x16 (&dv)[D / 32], const BwdCtx& cx, int q0, int my_key,
-                                          bool masked, int rows_first, int rows_count, int lane) {
+                                          bool masked, int rows_first, int rows_count,
+                                          const int* docq_t, bool has_doc, int my_doc, int lane) {
   using C = KVCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
@@ -210,15 +211,25 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
       }
     }
   if (masked) {
+    // rows [rows_first, rows_first + rows_count) may see this key (window and
+    // bounds); with a document mask the row's document must be the key's.
     const uint32_t span = static_cast<uint32_t>(rows_count);
     const int ib = q0 + 4 * g - rows_first;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool ok = static_cast<uint32_t>(ib + roff(qb, r)) < span;
-        s[qb][r] = ok ? s[qb][r] : 0.0f;
-        dp[qb][r] = ok ? dp[qb][r] : 0.0f;
+      for (int rr = 0; rr < 4; ++rr) {
+        int4 d4 = make_int4(0, 0, 0, 0);
+        if (has_doc) d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
+        const int dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          bool ok = static_cast<uint32_t>(ib + roff(qb, r)) < span;
+          if (has_doc) ok = ok && dv4[e] == my_doc;
+          s[qb][r] = ok ? s[qb][r] : 0.0f;
+          dp[qb][r] = ok ? dp[qb][r] : 0.0f;
+        }
       }
   }
   bf16x8 pf[2][2], sf[2][2];
@@ -266,6 +277,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   __shared__ __attribute__((aligned(16))) float lg0[C::BM];
   __shared__ __attribute__((aligned(16))) float lg1[C::BM];
   __shared__ __attribute__((aligned(16))) float lg2[C::BM];
+  __shared__ __attribute__((aligned(16))) int lz0[C::BM];
+  __shared__ __attribute__((aligned(16))) int lz1[C::BM];
+  __shared__ __attribute__((aligned(16))) int lz2[C::BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,35 +318,67 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
 
-  // Query tiles that meet the workgroup's keys: rows i with lo(i) <= last key
-  // and hi(i) >= first key.
+  // Query tiles that meet the workgroup's keys.  Dense: rows i with
+  // lo(i) <= last key and hi(i) >= first key, one interval.  Block-sparse:
+  // the FULL then the PARTIAL query blocks (128 rows = two tiles) listed for
+  // the mask's key block holding these keys.
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
-  const int c0 = kt * C::BN, c1 = min(a.Sk, c0 + C::BN) - 1;
-  int i_lo = 0, i_hi = a.Sq - 1;
-  if (win.R != kUnbounded) i_lo = max(i_lo, c0 - cx.delta_pos - win.R);
-  if (win.L != kUnbounded) i_hi = min(i_hi, c1 - cx.delta_pos + win.L);
-  const int qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
-  const int ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
+  const bool sparse = a.tiles.q_num_full != nullptr;
+  int qt_begin = 0, ntiles = 0, n_full_blk = 0;
+  const int32_t* qi_full = nullptr;
+  const int32_t* qi_part = nullptr;
+  if (sparse) {
+    const int u = b * a.tiles.nK + (kt * C::BN) / a.tiles.block_n;
+    n_full_blk = a.tiles.q_num_full[u];
+    ntiles = 2 * (n_full_blk + a.tiles.q_num_partial[u]);
+    qi_full = a.tiles.q_idx_full + (int64_t)u * a.tiles.nQ;
+    qi_part = a.tiles.q_idx_partial + (int64_t)u * a.tiles.nQ;
+  } else {
+    const int c0 = kt * C::BN, c1 = min(a.Sk, c0 + C::BN) - 1;
+    int i_lo = 0, i_hi = a.Sq - 1;
+    if (win.R != kUnbounded) i_lo = max(i_lo, c0 - cx.delta_pos - win.R);
+    if (win.L != kUnbounded) i_hi = min(i_hi, c1 - cx.delta_pos + win.L);
+    qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
+    ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
+  }
+  auto qt_of = [&](int t) -> int {
+    if (!sparse) return qt_begin + t;
+    const int blk = t >> 1;
+    return 2 * (blk < n_full_blk ? qi_full[blk] : qi_part[blk - n_full_blk]) + (t & 1);
+  };
   int rows_first, rows_count;
   win.key_rows(my_key, &rows_first, &rows_count);
+  const bool has_doc = a.mask.doc_q != nullptr;
+  const int my_doc = has_doc && k_ok ? a.mask.doc_k[(int64_t)b * a.Sk + my_key] : 0;
+  const int32_t* docq = has_doc ? a.mask.doc_q + (int64_t)b * a.Sq : nullptr;
 
   // Every wave issues the same number of memory operations per tile (its
-  // share of the Q and dO rows, plus one 64-float row: lse2 for even waves,
-  // Delta for odd ones -- waves 2 and 3 repeat waves 0 and 1), so one
-  // counter value means "all but the newest tile have landed".
+  // share of the Q and dO rows, plus one 64-entry row: lse2 for wave 0, Delta
+  // for waves 1 and 3, the rows' document ids for wave 2 when a document mask
+  // is given, else lse2 again), so one counter value means "all but the
+  // newest tile have landed".
   constexpr int kOpsPerTile = 2 * (64 / C::L::RG / 4) + 1;
   auto load_tile = [&](int qt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
-    float* ld = (wave & 1) ? (BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2))
-                           : (BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2));
     tile_dma<D>(reinterpret_cast<bf16_t*>(qd), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
     tile_dma<D>(reinterpret_cast<bf16_t*>(dd), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
     // rows past Sq repeat the last row; they are masked on partial tiles
     const int i = min(qt * C::BM + lane, a.Sq - 1);
-    __builtin_amdgcn_global_load_lds((wave & 1) ? dlp + i : lsep + i,
-                                     (__attribute__((address_space(3))) void*)ld, 4, 0, 0);
+    const void* src;
+    void* dst;
+    if (wave & 1) {
+      src = dlp + i;
+      dst = BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2);
+    } else if (wave == 2 && has_doc) {
+      src = docq + i;
+      dst = BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2);
+    } else {
+      src = lsep + i;
+      dst = BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2);
+    }
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
   };
   auto wait_older = [&](bool newest_in_flight) {
     if (newest_in_flight) {
@@ -356,8 +402,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       dk[db][r] = 0.0f;
     }
 
-  if (ntiles > 0) load_tile(qt_begin, B0{});
-  if (ntiles > 1) load_tile(qt_begin + 1, B1{});
+  if (ntiles > 0) load_tile(qt_of(0), B0{});
+  if (ntiles > 1) load_tile(qt_of(1), B1{});
   wait_older(ntiles > 1);
   __syncthreads();
 
@@ -365,15 +411,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   auto step = [&](int t, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     using AHEAD = std::integral_constant<int, (BUF + 2) % 3>;
-    const int qt = qt_begin + t;
+    const int qt = qt_of(t);
     const bool ahead = t + 2 < ntiles;
-    if (ahead) load_tile(qt + 2, AHEAD{});
-    const TileRange trq(win, qt, C::BM, 32);
-    if (kw >= trq.kt_begin && kw < trq.kt_end)
+    if (ahead) load_tile(qt_of(t + 2), AHEAD{});
+    bool run, masked;
+    if (sparse) {
+      run = true;
+      masked = (t >> 1) >= n_full_blk;
+    } else {
+      const TileRange trq(win, qt, C::BM, 32);
+      run = kw >= trq.kt_begin && kw < trq.kt_end;
+      masked = !trq.full(kw);
+    }
+    if (run)
       dkdv_tile<D, MOD>(BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2), BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2),
                         BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2), BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2),
-                        kf, vf, dk, dv, cx, qt * C::BM, my_key, !trq.full(kw), rows_first, rows_count,
-                        lane);
+                        kf, vf, dk, dv, cx, qt * C::BM, my_key, masked, rows_first, rows_count,
+                        BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2), has_doc, my_doc, lane);
     wait_older(ahead);  // tile t + 1 has landed
     __syncthreads();
   };
@@ -455,7 +509,8 @@ template <int D, int MOD, bool MASKED>
 __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32],
                                         const BwdCtx& cx, float lse2, float dl, int my_q, int key_base,
-                                        int row_first, int row_count, int lane) {
+                                        int row_first, int row_count, const int* dock_t, bool has_doc,
+                                        int my_doc, int lane) {
   using C = QCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
@@ -488,14 +543,25 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float th = 0.0f;
-      const int j = key_base + 4 * g + roff(kb, r);
-      float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[kb][r], lse2, cx, my_q + cx.delta_pos - j, &th));
-      if (MASKED) p = static_cast<uint32_t>(jb + roff(kb, r)) < span ? p : 0.0f;
-      float dsv = p * (dp[kb][r] - dl);
-      if (kSoftcap) dsv *= 1.0f - th * th;
-      sf[kb][r >> 3][r & 7] = static_cast<__bf16>(dsv);
+    for (int rr = 0; rr < 4; ++rr) {
+      int4 d4 = make_int4(0, 0, 0, 0);
+      if (MASKED && has_doc) d4 = *reinterpret_cast<const int4*>(dock_t + 32 * kb + 8 * rr + 4 * g);
+      const int dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rr + e;
+        float th = 0.0f;
+        const int j = key_base + 4 * g + roff(kb, r);
+        float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[kb][r], lse2, cx, my_q + cx.delta_pos - j, &th));
+        if (MASKED) {
+          bool ok = static_cast<uint32_t>(jb + roff(kb, r)) < span;
+          if (has_doc) ok = ok && dv4[e] == my_doc;
+          p = ok ? p : 0.0f;
+        }
+        float dsv = p * (dp[kb][r] - dl);
+        if (kSoftcap) dsv *= 1.0f - th * th;
+        sf[kb][r >> 3][r & 7] = static_cast<__bf16>(dsv);
+      }
     }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -514,6 +580,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lk1[C::TB];
   __shared__ __attribute__((aligned(16))) char lv0[C::TB];
   __shared__ __attribute__((aligned(16))) char lv1[C::TB];
+  __shared__ __attribute__((aligned(16))) int lz0[C::BN];
+  __shared__ __attribute__((aligned(16))) int lz1[C::BN];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -554,17 +622,49 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     dl = a.delta[((int64_t)b * a.Hq + h) * a.Sq + my_q];
   }
 
+  // Key tiles in processing order, FULL ones first.  Dense: the interval of
+  // the causal / window band.  Block-sparse: the mask's FULL then PARTIAL
+  // key blocks of this query block (block_n / 64 tiles each).
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
   const TileRange range(win, qt, C::BM, C::BN);
-  const int ntiles = range.kt_end - range.kt_begin;
-  const int nfull = range.n_full();
+  const bool sparse = a.tiles.kv_num_full != nullptr;
+  int ntiles, nfull, n_full_blk = 0, sub = 1;
+  const int32_t* ki_full = nullptr;
+  const int32_t* ki_part = nullptr;
+  if (sparse) {
+    const int row = b * a.tiles.nQ + qt;
+    sub = a.tiles.block_n / C::BN;
+    n_full_blk = a.tiles.kv_num_full[row];
+    ntiles = (n_full_blk + a.tiles.kv_num_partial[row]) * sub;
+    nfull = n_full_blk * sub;
+    ki_full = a.tiles.kv_idx_full + (int64_t)row * a.tiles.nK;
+    ki_part = a.tiles.kv_idx_partial + (int64_t)row * a.tiles.nK;
+  } else {
+    ntiles = range.kt_end - range.kt_begin;
+    nfull = range.n_full();
+  }
+  auto kt_of = [&](int t) -> int {
+    if (!sparse) return range.kt_at(t);
+    const int blk = t / sub;
+    return (blk < n_full_blk ? ki_full[blk] : ki_part[blk - n_full_blk]) * sub + t % sub;
+  };
   int row_first, row_count;
   win.row_keys(my_q, &row_first, &row_count);
+  const bool has_doc = a.mask.doc_q != nullptr;
+  const int my_doc = has_doc && q_ok ? a.mask.doc_q[(int64_t)b * a.Sq + my_q] : 0;
+  const int32_t* dock = has_doc ? a.mask.doc_k + (int64_t)b * a.Sk : nullptr;
 
+  // K and V of tile kt into buffer BUF, and (document masks) the tile's 64
+  // key document ids, copied by wave 0; every wait below is a full one.
   auto load_tile = [&](int kt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lk1 : lk0), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
     tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lv1 : lv0), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
+    if (has_doc && wave == 0) {
+      const int j = min(kt * C::BN + lane, a.Sk - 1);  // keys past Sk are masked
+      __builtin_amdgcn_global_load_lds(dock + j, (__attribute__((address_space(3))) void*)(BUF ? lz1 : lz0),
+                                       4, 0, 0);
+    }
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -575,18 +675,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
 
-  if (ntiles > 0) load_tile(range.kt_at(0), B0{});
+  if (ntiles > 0) load_tile(kt_of(0), B0{});
   wait_dma();
   __syncthreads();
 
   auto step = [&](int t, auto buf_tag, auto masked) {
     constexpr int BUF = decltype(buf_tag)::value;
     using NEXT = std::integral_constant<int, 1 - BUF>;
-    const int kt = range.kt_at(t);
+    const int kt = kt_of(t);
     const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(range.kt_at(t + 1), NEXT{});
+    if (has_next) load_tile(kt_of(t + 1), NEXT{});
     dq_tile<D, MOD, decltype(masked)::value>(BUF ? lk1 : lk0, BUF ? lv1 : lv0, qf, df, dq, cx, lse2, dl,
-                                             my_q, kt * C::BN, row_first, row_count, lane);
+                                             my_q, kt * C::BN, row_first, row_count, BUF ? lz1 : lz0,
+                                             has_doc, my_doc, lane);
     wait_dma();
     __syncthreads();
   };

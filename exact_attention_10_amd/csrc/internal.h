@@ -55,6 +55,17 @@ constexpr int kFwdF32BM = 64;
 constexpr int kFwdF32BN = 64;
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 
+// Block-sparse tile lists for the backward: per query block the key blocks
+// (dQ), per key block the query blocks (dK/dV); mask tiles of 128 query rows
+// by block_n keys, block_n a multiple of 128.
+struct BwdTiles {
+  const int32_t* kv_num_full; const int32_t* kv_idx_full;
+  const int32_t* kv_num_partial; const int32_t* kv_idx_partial;
+  const int32_t* q_num_full; const int32_t* q_idx_full;
+  const int32_t* q_num_partial; const int32_t* q_idx_partial;
+  int nQ, nK, block_n;
+};
+
 struct BwdArgs {
   const void* q; const void* k; const void* v; const void* o; const void* dout;
   const float* lse;
@@ -73,6 +84,7 @@ struct BwdArgs {
   int64_t alibi_sb;
   float softcap;
   MaskArgs mask;
+  BwdTiles tiles;            // block-sparse lists (kv_num_full == nullptr: dense)
   float* delta;              // workspace [B, Hq, Sq]
   float* lse2;               // workspace [B, Hq, Sq]: lse * log2(e), +inf for empty rows
   float* part_dk;            // workspace [B, Sk, Hq, D] (grouped heads only)

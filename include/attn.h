@@ -189,8 +189,15 @@ attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype,
  *             element is reduced in a fixed order without atomics, so
  *             repeated calls are bitwise identical).
  *   workspace : at least attn_bwd_workspace_size(p) bytes, 256-byte aligned.
- * Errors: as attn_fwd; UNSUPPORTED for fp32 inputs, block masks or
- * deterministic == 0; WORKSPACE if too small. */
+ *   p->block_mask : as in attn_fwd ([GYM] block mask, [FX4] block sparsity);
+ *             the dK/dV pass walks each key block's query-block lists (FULL
+ *             first, then PARTIAL), the dQ pass each query block's key-block
+ *             lists; the predicate (causal / window / document) is evaluated
+ *             on PARTIAL tiles only.  Needs block_m == 128, block_n a multiple
+ *             of 128 and the query-block lists of block_mask_build().
+ * Errors: as attn_fwd; UNSUPPORTED for fp32 inputs, a block mask whose
+ * block_n is not a multiple of 128, or deterministic == 0; WORKSPACE if too
+ * small. */
 attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k,
                      attn_tensor v, attn_tensor o, attn_tensor dout,
                      const float* lse, attn_tensor dq, attn_tensor dk,

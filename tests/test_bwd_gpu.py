@@ -83,3 +83,78 @@ def test_bwd_llama8b_full(b):
     check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
     dq2, dk2, dv2 = run_bwd(b, w, **kw)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse backward ([GYM] create_block_mask; [FX4] block sparsity): the
+# dK/dV kernel walks each key block's query-block lists, the dQ kernel each
+# query block's key-block lists; partial tiles evaluate the predicate.
+
+SPARSE_CASES = [
+    # B, S, Hq, Hkv, D, block_n, causal, window, doc length range, options
+    (2, 300, 4, 2, 64, 128, True, (-1, -1), (20, 90), {}),
+    (1, 333, 2, 2, 128, 256, False, (-1, -1), (30, 200), {"softcap": 3.0}),
+    (1, 257, 8, 2, 128, 128, True, (-1, -1), None, {}),
+    (1, 400, 4, 1, 64, 128, True, (100, 0), None, {"alibi": True}),
+    (2, 520, 4, 4, 128, 128, True, (-1, -1), (64, 300), {"scale": -0.08}),
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=[str(i) for i in range(len(SPARSE_CASES))])
+def test_bwd_block_sparse(b, case):
+    B, S, Hq, Hkv, D, bn, causal, window, doc_range, opt = case
+    w = inputs.random_case(700 + S + D, B, S, S, Hq, Hkv, D, dtype="bf16", grad=True,
+                           doc_len_range=doc_range)
+    doc = w.get("doc")
+    doc_t = torch.from_numpy(doc).cuda() if doc is not None else None
+    m = b.block_mask_build(B, S, S, 128, bn, causal=causal, window=window, doc_q=doc_t, doc_k=doc_t)
+    kw = dict(softmax_scale=opt.get("scale", 0.12), softcap=opt.get("softcap", 0.0), block_mask=m)
+    slopes = None
+    if opt.get("alibi"):
+        slopes = np.exp2(-8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+    dq, dk, dv = run_bwd(b, w, **kw)
+    rq, rk, rv = oracle.attention_bwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), f64(w, "do"),
+                                      scale=kw["softmax_scale"], causal=causal, window=window,
+                                      alibi_slopes=slopes, softcap=kw["softcap"], doc_q=doc, doc_k=doc)
+    check_o(to_f64(dq), rq, GRAD_ATOL, "dQ")
+    check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
+
+
+def test_bwd_doc_mask_s8192(b):
+    """The packed-document workload (B=2, H=16, S=8192, D=64, causal within
+    documents, 128x128 blocks) through the block-sparse backward.  Documents
+    do not interact, so the oracle is run per document on four heads (the
+    pinned per-document identity) and compared with those slices."""
+    w = inputs.doc_mask()
+    rng = np.random.default_rng(44)
+    w["do"] = inputs.f32_to_bf16_bits(rng.standard_normal(w["q"].shape, dtype=np.float32))
+    doc = torch.from_numpy(w["doc"]).cuda()
+    m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
+    dq, dk, dv = run_bwd(b, w, softmax_scale=w["scale"], block_mask=m)
+    got = [to_f64(t) for t in (dq, dk, dv)]
+    heads = [0, 5, 10, 15]
+    x = {n: f64(w, n)[:, :, heads] for n in ("q", "k", "v", "do")}
+    for bb in range(2):
+        s0 = 0
+        for n in w["doc_lengths"][bb]:
+            sl = slice(s0, s0 + n)
+            ref = oracle.attention_bwd(x["q"][bb:bb + 1, sl], x["k"][bb:bb + 1, sl],
+                                       x["v"][bb:bb + 1, sl], x["do"][bb:bb + 1, sl],
+                                       scale=w["scale"], causal=True)
+            for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+                check_o(g[bb:bb + 1, sl][:, :, heads], r, GRAD_ATOL, "%s b%d doc@%d" % (name, bb, s0))
+            s0 += n
+
+
+def test_bwd_block_sparse_errors(b):
+    w = inputs.random_case(5, 1, 256, 256, 2, 2, 64, dtype="bf16", grad=True)
+    q, k, v, do = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v", "do"))
+    m64 = b.block_mask_build(1, 256, 256, 128, 64, causal=True)
+    o, lse = b.attn_fwd(q, k, v, block_mask=m64)
+    with pytest.raises(b.AttnError):  # block_n = 64 is forward-only
+        b.attn_bwd(q, k, v, o, do, lse, block_mask=m64)
+    m = b.block_mask_build(1, 256, 256, 128, 128, causal=True)
+    with pytest.raises(b.AttnError):  # the block mask carries the predicate
+        b.attn_bwd(q, k, v, o, do, lse, causal=True, block_mask=m)
