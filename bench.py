@@ -214,6 +214,27 @@ def main():
         "kernels": kernels,
     }
 
+    # the same backward with deterministic=0 (dQ by fp32 atomic adds in the
+    # dK/dV kernel, then a scale-and-round pass): per-stage times
+    nd_args = bwd_args[:10] + (0,) + bwd_args[11:]
+    nd = [Prepared(lib.attn_bwd_stage, nd_args + (st, stream)) for st in range(4)]
+    nd_ev = []
+    for rep in range(7):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        for i, st in enumerate(nd):
+            ev[i].record()
+            st()
+        ev[4].record()
+        if rep >= 2:
+            nd_ev.append(ev)
+    torch.cuda.synchronize()
+    nd_ms = [float(np.median([e[i].elapsed_time(e[i + 1]) for e in nd_ev])) for i in range(4)]
+    out["bwd_deterministic0"] = {
+        "stage_ms": dict(zip(["delta_and_zero", "dkdv_with_atomic_dq", "group_sum", "dq_convert"],
+                             [round(x, 5) for x in nd_ms])),
+        "total_ms": round(sum(nd_ms), 5),
+        "deterministic1_total_ms": round(bwd_ms, 5)}
+
     del ws, dq, dk, dv
     if not args.no_extra:
         out["extra"] = extra_workloads(b, lib, inputs, torch, np, dev, to_dev)
@@ -397,10 +418,23 @@ def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
                                                  out=oo, lse=ll), 10)
     pairs = sum(n * (n + 1) // 2 for lens_b in w["doc_lengths"] for n in lens_b)
     fl = 4.0 * 16 * 64 * pairs
+    # block-sparse backward on the same mask (dO: seeded normals, seed 44)
+    rng = np.random.default_rng(44)
+    do = to_dev(inputs.f32_to_bf16_bits(rng.standard_normal(w["q"].shape, dtype=np.float32)))
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pb = b._params(q, k, 64, w["scale"], False, (-1, -1), None, 0.0, m)
+    wsb = torch.empty(lib.attn_bwd_workspace_size(ctypes.byref(pb)), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bwd_call = Prepared(lib.attn_bwd, (ctypes.byref(pb), b._tensor(q), b._tensor(k), b._tensor(v),
+                                       b._tensor(oo), b._tensor(do), b._ptr(ll), b._tensor(gq),
+                                       b._tensor(gk), b._tensor(gv), 1, b._ptr(wsb), wsb.numel(), stream))
+    med_b, _ = timed(torch, np, bwd_call, 10)
     ex["doc_mask_s8192_d64"] = {"block_mask_build_ms": round(med_m, 4), "fwd_ms": round(med, 4),
                                 "tflops": round(fl / (med * 1e-3) / 1e12, 2),
                                 "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 /
-                                                           PEAK_BF16_TFLOPS, 4)}
+                                                           PEAK_BF16_TFLOPS, 4),
+                                "bwd_ms": round(med_b, 4),
+                                "bwd_tflops_counted": round(2.5 * fl / (med_b * 1e-3) / 1e12, 2)}
     return ex
 
 

@@ -254,8 +254,8 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
         bm->q_idx_partial == nullptr)
       return fail(ATTN_ERR_INVALID_ARG, "block mask query lists are NULL (attn_bwd needs them)");
   }
-  if (deterministic != 1)
-    return fail(ATTN_ERR_UNSUPPORTED, "only the deterministic backward (deterministic=1) is implemented");
+  if (deterministic != 0 && deterministic != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "deterministic must be 0 or 1 (got %d)", deterministic);
   const size_t need = attn_bwd_workspace_size(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "attn_bwd needs %zu workspace bytes, got %zu", need, workspace_bytes);
@@ -302,6 +302,8 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
   const size_t part = up((size_t)p->B * p->Sk * p->Hq * p->D * sizeof(float));
   a.part_dk = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest) : nullptr;
   a.part_dv = p->Hq / p->Hkv > 1 ? reinterpret_cast<float*>(rest + part) : nullptr;
+  if (p->Hq / p->Hkv > 1) rest += 2 * part;
+  a.dq_acc = deterministic ? nullptr : reinterpret_cast<float*>(rest);
   return hip_status(attn::launch_bwd_bf16(a, stage_mask, static_cast<hipStream_t>(stream)), "attn_bwd launch");
 }
 

@@ -69,6 +69,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (a.dq_acc != nullptr && row < rows) {
+    // the non-deterministic dQ accumulator of this row starts at zero
+    float4* z = reinterpret_cast<float4*>(a.dq_acc + row * D + part * 8);
+    z[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    z[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
   if (row < rows && part == 0) {
     const int64_t idx = ((int64_t)b * a.Hq + h) * a.Sq + i;
     a.delta[idx] = acc;
@@ -151,16 +157,30 @@ struct KVCfg {
   static constexpr int DBLK = D / 32;
 };
 
-// One 64-query tile against this wave's 32 keys.  S = Q K^T and dP = dO V^T
-// give one key per lane (queries along the accumulator registers), so P and
-// dS rounded to bf16 are the A operands of dV += P^T dO and dK += dS^T Q.
+// Stores this lane's dS (key row key_row, 64 query columns) into a
+// TileLayout<64> image of dS^T for the dQ product.
+__device__ __forceinline__ void store_ds(char* ds_lds, const bf16x8 (&sf)[2][2], int key_row, int g) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 w = __builtin_bit_cast(uint4, sf[qb][m >> 1]);
+      const uint2 h = (m & 1) ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);
+      *reinterpret_cast<uint2*>(ds_lds + TileLayout<64>::off(key_row, 4 * qb + m) + 8 * g) = h;
+    }
+}
+
+// One 64-query tile against this wave's 32 keys, first half: S = Q K^T and
+// dP = dO V^T give one key per lane (queries along the accumulator
+// registers); P and dS rounded to bf16 come out as pf / sf, which are the A
+// operands of dV += P^T dO and dK += dS^T Q (dkdv_accum).
 template <int D, int MOD>
-__device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_lds, const float* lse_t,
-                                          const float* dl_t, const bf16x8 (&kf)[D / 16],
-                                          const bf16x8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
-                                          f32x16 (&dv)[D / 32], const BwdCtx& cx, int q0, int my_key,
-                                          bool masked, int rows_first, int rows_count,
-                                          const int* docq_t, bool has_doc, int my_doc, int lane) {
+__device__ __forceinline__ void dkdv_scores(const char* qt_lds, const char* dot_lds, const float* lse_t,
+                                            const float* dl_t, const bf16x8 (&kf)[D / 16],
+                                            const bf16x8 (&vf)[D / 16], const BwdCtx& cx, int q0,
+                                            int my_key, bool masked, int rows_first, int rows_count,
+                                            const int* docq_t, bool has_doc, int my_doc,
+                                            bf16x8 (&pf)[2][2], bf16x8 (&sf)[2][2], int lane) {
   using C = KVCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
@@ -232,7 +252,6 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
         }
       }
   }
-  bf16x8 pf[2][2], sf[2][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -240,8 +259,15 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
       pf[qb][r >> 3][r & 7] = static_cast<__bf16>(s[qb][r]);
       sf[qb][r >> 3][r & 7] = static_cast<__bf16>(dp[qb][r]);
     }
+}
 
-  // dV += P^T dO ; dK += dS^T Q  (the D/32 output blocks are independent)
+// Second half: dV += P^T dO ; dK += dS^T Q (the D/32 output blocks are
+// independent), with transposed reads of the dO and Q tiles.
+template <int D>
+__device__ __forceinline__ void dkdv_accum(const char* qt_lds, const char* dot_lds, const bf16x8 (&pf)[2][2],
+                                           const bf16x8 (&sf)[2][2], f32x16 (&dk)[D / 32],
+                                           f32x16 (&dv)[D / 32], int lane) {
+  using C = KVCfg<D>;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     bf16x8 fo[C::DBLK], fq[C::DBLK];
@@ -258,7 +284,7 @@ __device__ __forceinline__ void dkdv_tile(const char* qt_lds, const char* dot_ld
   }
 }
 
-template <int D, int MOD>
+template <int D, int MOD, bool kDq>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial) {
   using C = KVCfg<D>;
   // Three buffers (one workgroup per CU leaves the LDS room): the copies of
@@ -280,6 +306,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   __shared__ __attribute__((aligned(16))) int lz0[C::BM];
   __shared__ __attribute__((aligned(16))) int lz1[C::BM];
   __shared__ __attribute__((aligned(16))) int lz2[C::BM];
+  // dQ in this kernel (non-deterministic variant): the workgroup's 128 K rows
+  // and each tile's dS^T (128 keys x 64 queries) in LDS.
+  __shared__ __attribute__((aligned(16))) char lkk[kDq ? 2 * C::TB : 16];
+  __shared__ __attribute__((aligned(16))) char lds_s[kDq ? 2 * TileLayout<64>::BYTES : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   // the FULL then the PARTIAL query blocks (128 rows = two tiles) listed for
   // the mask's key block holding these keys.
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
-  const bool sparse = a.tiles.q_num_full != nullptr;
+  constexpr bool sparse = (MOD & 4) != 0;  // block-mask lists (else the dense band)
   int qt_begin = 0, ntiles = 0, n_full_blk = 0;
   const int32_t* qi_full = nullptr;
   const int32_t* qi_part = nullptr;
@@ -348,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   };
   int rows_first, rows_count;
   win.key_rows(my_key, &rows_first, &rows_count);
-  const bool has_doc = a.mask.doc_q != nullptr;
+  const bool has_doc = sparse && a.mask.doc_q != nullptr;  // document masks come with block masks
   const int my_doc = has_doc && k_ok ? a.mask.doc_k[(int64_t)b * a.Sk + my_key] : 0;
   const int32_t* docq = has_doc ? a.mask.doc_q + (int64_t)b * a.Sq : nullptr;
 
@@ -402,10 +432,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       dk[db][r] = 0.0f;
     }
 
+  if constexpr (kDq) {
+    tile_dma<D>(reinterpret_cast<bf16_t*>(lkk), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(lkk + C::TB), kp, a.k_ss, kt * C::BN + 64, a.Sk, wave, lane);
+  }
   if (ntiles > 0) load_tile(qt_of(0), B0{});
   if (ntiles > 1) load_tile(qt_of(1), B1{});
-  wait_older(ntiles > 1);
+  wait_older(ntiles > 1);  // also covers the K copies, issued first
   __syncthreads();
+
+  // dQ rows of tile qt += dS K over the workgroup's 128 keys: wave w owns
+  // query block w % 2 and D/64 of the 32-column blocks; fp32 atomic adds
+  // into the accumulator (rows past Sq skipped; their dS is zero anyway).
+  float* dq_row0 = kDq ? a.dq_acc + ((int64_t)b * a.Sq * a.Hq + h) * D : nullptr;
+  auto dq_update = [&](int qt) {
+    constexpr int NDB = C::DBLK / 2 > 0 ? C::DBLK / 2 : 1;
+    const int qblk = wave & 1;
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int j = 0; j < NDB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 af = tr_frag<64>(lds_s, kk, qblk, lane);
+#pragma unroll
+      for (int j = 0; j < NDB; ++j)
+        acc[j] = mfma32(af, tr_frag<D>(lkk, kk, NDB * (wave >> 1) + j, lane), acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      const int d = 32 * (NDB * (wave >> 1) + j) + c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = qt * C::BM + 32 * qblk + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (i < a.Sq) unsafeAtomicAdd(dq_row0 + (int64_t)i * a.Hq * D + d, acc[j][r]);
+      }
+    }
+  };
 
   const int kw = kv0 / 32;  // this wave's 32-key block index
   auto step = [&](int t, auto buf_tag) {
@@ -423,13 +487,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       run = kw >= trq.kt_begin && kw < trq.kt_end;
       masked = !trq.full(kw);
     }
-    if (run)
-      dkdv_tile<D, MOD>(BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2), BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2),
-                        BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2), BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2),
-                        kf, vf, dk, dv, cx, qt * C::BM, my_key, masked, rows_first, rows_count,
-                        BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2), has_doc, my_doc, lane);
+    const char* qbuf = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
+    const char* dbuf = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
+    bf16x8 pf[2][2], sf[2][2];
+    auto scores = [&]() {
+      dkdv_scores<D, MOD>(qbuf, dbuf, BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2),
+                          BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2), kf, vf, cx, qt * C::BM, my_key, masked,
+                          rows_first, rows_count, BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2), has_doc, my_doc,
+                          pf, sf, lane);
+    };
+    if constexpr (!kDq) {
+      if (run) {
+        scores();
+        dkdv_accum<D>(qbuf, dbuf, pf, sf, dk, dv, lane);
+      }
+    } else {
+      if (run) scores();
+      if (!run) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sf[x][y][e] = static_cast<__bf16>(0.0f);
+      }
+      __syncthreads();  // every wave has finished reading the previous dS^T
+      store_ds(lds_s, sf, 32 * wave + c, g);
+      if (run) dkdv_accum<D>(qbuf, dbuf, pf, sf, dk, dv, lane);
+    }
     wait_older(ahead);  // tile t + 1 has landed
-    __syncthreads();
+    __syncthreads();    // ... for every wave; with kDq also: dS^T is complete
+    if constexpr (kDq) dq_update(qt);
   };
   int t = 0;
   for (; t + 2 < ntiles; t += 3) {
@@ -488,6 +576,29 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs a) {
   bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)j * a.dv_ss + g * a.dv_sh;
   dkp[d] = f32_to_bf16(sk);
   dvp[d] = f32_to_bf16(sv);
+}
+
+// Non-deterministic dQ: scale the fp32 accumulator and round to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdArgs a) {
+  const int64_t n = (int64_t)a.B * a.Sq * a.Hq * (D / 8);
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int part = static_cast<int>(t % (D / 8));
+  const int64_t row = t / (D / 8);  // (b * Sq + i) * Hq + h
+  const int h = static_cast<int>(row % a.Hq);
+  const int i = static_cast<int>((row / a.Hq) % a.Sq);
+  const int b = static_cast<int>(row / ((int64_t)a.Hq * a.Sq));
+  const float4* src = reinterpret_cast<const float4*>(a.dq_acc + row * D + part * 8);
+  const float4 x = src[0], y = src[1];
+  const float sc = a.scale;
+  uint4 o;
+  o.x = f32_to_bf16(x.x * sc) | (uint32_t)f32_to_bf16(x.y * sc) << 16;
+  o.y = f32_to_bf16(x.z * sc) | (uint32_t)f32_to_bf16(x.w * sc) << 16;
+  o.z = f32_to_bf16(y.x * sc) | (uint32_t)f32_to_bf16(y.y * sc) << 16;
+  o.w = f32_to_bf16(y.z * sc) | (uint32_t)f32_to_bf16(y.w * sc) << 16;
+  *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.dq) + b * a.dq_sb + (int64_t)i * a.dq_ss + h * a.dq_sh +
+                            part * 8) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -627,7 +738,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // key blocks of this query block (block_n / 64 tiles each).
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
   const TileRange range(win, qt, C::BM, C::BN);
-  const bool sparse = a.tiles.kv_num_full != nullptr;
+  constexpr bool sparse = (MOD & 4) != 0;  // block-mask lists (else the dense band)
   int ntiles, nfull, n_full_blk = 0, sub = 1;
   const int32_t* ki_full = nullptr;
   const int32_t* ki_part = nullptr;
@@ -650,7 +761,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
   int row_first, row_count;
   win.row_keys(my_q, &row_first, &row_count);
-  const bool has_doc = a.mask.doc_q != nullptr;
+  const bool has_doc = sparse && a.mask.doc_q != nullptr;  // document masks come with block masks
   const int my_doc = has_doc && q_ok ? a.mask.doc_q[(int64_t)b * a.Sq + my_q] : 0;
   const int32_t* dock = has_doc ? a.mask.doc_k + (int64_t)b * a.Sk : nullptr;
 
@@ -728,8 +839,12 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int partial = G > 1 ? 1 : 0;
   const int nkt = (a.Sk + KVCfg<D>::BN - 1) / KVCfg<D>::BN;
+  const bool atomic_dq = a.dq_acc != nullptr;
   if ((stages & 2) && nkt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MOD>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
+    if (atomic_dq)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, MOD, true>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -741,7 +856,12 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   }
   const int nqt = (a.Sq + QCfg<D>::BM - 1) / QCfg<D>::BM;
   if (!(stages & 8) || nqt == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, MOD>), dim3(nqt * a.Hq * a.B), dim3(256), 0, s, a);
+  if (atomic_dq) {
+    const int64_t n = (int64_t)a.B * a.Sq * a.Hq * (D / 8);
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MOD>), dim3(nqt * a.Hq * a.B), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -754,12 +874,18 @@ hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0);
+  // bit 0 ALiBi, bit 1 softcap, bit 2 block-sparse lists (document ids only with these)
+  const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0) |
+                  (a.tiles.kv_num_full != nullptr ? 4 : 0);
   switch (mod) {
     case 0: return launch_mod<D, 0>(a, stages, s);
     case 1: return launch_mod<D, 1>(a, stages, s);
     case 2: return launch_mod<D, 2>(a, stages, s);
-    default: return launch_mod<D, 3>(a, stages, s);
+    case 3: return launch_mod<D, 3>(a, stages, s);
+    case 4: return launch_mod<D, 4>(a, stages, s);
+    case 5: return launch_mod<D, 5>(a, stages, s);
+    case 6: return launch_mod<D, 6>(a, stages, s);
+    default: return launch_mod<D, 7>(a, stages, s);
   }
 }
 
@@ -769,6 +895,7 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t n = 2 * up((size_t)B * Hq * Sq * sizeof(float));  // Delta, lse2
   if (Hkv > 0 && Hq / Hkv > 1) n += 2 * up((size_t)B * Sk * Hq * D * sizeof(float));
+  n += up((size_t)B * Sq * Hq * D * sizeof(float));  // non-deterministic dQ accumulator
   return n;
 }
 

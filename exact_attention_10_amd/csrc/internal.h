@@ -89,6 +89,7 @@ struct BwdArgs {
   float* lse2;               // workspace [B, Hq, Sq]: lse * log2(e), +inf for empty rows
   float* part_dk;            // workspace [B, Sk, Hq, D] (grouped heads only)
   float* part_dv;
+  float* dq_acc;             // workspace [B, Sq, Hq, D]: non-deterministic dQ (nullptr: dQ kernel)
 };
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 // stage_mask bit k runs stage k (0 Delta, 1 dK/dV, 2 group sum, 3 dQ).

@@ -185,19 +185,27 @@ attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype,
  * sum the G query heads that read it.
  *   o, lse : the forward's outputs for the same inputs.
  *   dq, dk, dv : outputs, same shapes and dtype as q, k, v.
- *   deterministic : must be 1 (the only implemented schedule: every output
- *             element is reduced in a fixed order without atomics, so
- *             repeated calls are bitwise identical).
- *   workspace : at least attn_bwd_workspace_size(p) bytes, 256-byte aligned.
+ *   deterministic : 1 = every output element is reduced in a fixed order
+ *             without atomics (a separate dQ pass), so repeated calls are
+ *             bitwise identical.  0 = dQ is accumulated by the dK/dV pass
+ *             with fp32 atomic adds into the workspace and then scaled and
+ *             rounded (FA's non-deterministic schedule; dK, dV unchanged).
+ *             On gfx950 fp32 device atomics sustain only a few hundred G
+ *             adds/s, so 0 is the slower schedule here (about 4x on
+ *             B1 H32/8 S2048 D128 causal); 1 is the fast path.
+ *             Other values: INVALID_ARG.
+ *   workspace : at least attn_bwd_workspace_size(p) bytes, 256-byte aligned
+ *             (enough for either value of deterministic: Delta and the LSE in
+ *             exp2 units [B, Hq, Sq], fp32 per-head dK/dV partials
+ *             [B, Sk, Hq, D] x 2 when Hq > Hkv, fp32 dQ [B, Sq, Hq, D]).
  *   p->block_mask : as in attn_fwd ([GYM] block mask, [FX4] block sparsity);
  *             the dK/dV pass walks each key block's query-block lists (FULL
  *             first, then PARTIAL), the dQ pass each query block's key-block
  *             lists; the predicate (causal / window / document) is evaluated
  *             on PARTIAL tiles only.  Needs block_m == 128, block_n a multiple
  *             of 128 and the query-block lists of block_mask_build().
- * Errors: as attn_fwd; UNSUPPORTED for fp32 inputs, a block mask whose
- * block_n is not a multiple of 128, or deterministic == 0; WORKSPACE if too
- * small. */
+ * Errors: as attn_fwd; UNSUPPORTED for fp32 inputs or a block mask whose
+ * block_n is not a multiple of 128; WORKSPACE if too small. */
 attn_status attn_bwd(const attn_params* p, attn_tensor q, attn_tensor k,
                      attn_tensor v, attn_tensor o, attn_tensor dout,
                      const float* lse, attn_tensor dq, attn_tensor dk,
@@ -210,10 +218,12 @@ size_t attn_bwd_workspace_size(const attn_params* p);
  * stream (with the same workspace) is exactly attn_bwd:
  *   0  Delta_i = <dout_i, o_i> into the workspace
  *   1  dK/dV kernel (fp32 per-head partials in the workspace when Hq > Hkv,
- *      else dk/dv directly)
+ *      else dk/dv directly; with deterministic == 0 also the atomic dQ
+ *      accumulation, which stage 0 zeroes)
  *   2  sum of the per-head partials of each kv head into dk/dv, in head order
  *      (nothing to do when Hq == Hkv)
- *   3  dQ kernel (reads Delta)
+ *   3  dQ kernel (reads Delta); with deterministic == 0 the scale-and-round
+ *      of the dQ accumulator
  * Errors: as attn_bwd; INVALID_ARG for a stage outside 0..3. */
 attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
                            attn_tensor v, attn_tensor o, attn_tensor dout,

@@ -158,3 +158,63 @@ def test_bwd_block_sparse_errors(b):
     m = b.block_mask_build(1, 256, 256, 128, 128, causal=True)
     with pytest.raises(b.AttnError):  # the block mask carries the predicate
         b.attn_bwd(q, k, v, o, do, lse, causal=True, block_mask=m)
+
+
+# ---------------------------------------------------------------------------
+# deterministic=0 ([FA] deterministic flag): dQ accumulated by the dK/dV
+# kernel with fp32 atomic adds (summation order not fixed), then scaled and
+# rounded by a conversion pass.  Same gradients to the same tolerance.
+
+def run_bwd_nd(b, w, bwd_kw, **kw):
+    q, k, v, do = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v", "do"))
+    o, lse = b.attn_fwd(q, k, v, **kw)
+    dq, dk, dv = b.attn_bwd(q, k, v, o, do, lse, deterministic=False, **kw, **bwd_kw)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("case", [CASES[i] for i in (1, 2, 3, 5, 7, 9, 10)],
+                         ids=[str(i) for i in (1, 2, 3, 5, 7, 9, 10)])
+def test_bwd_nondeterministic(b, case):
+    B, Sq, Sk, Hq, Hkv, D, opt = case
+    w = inputs.random_case(300 + Sq + Sk + D, B, Sq, Sk, Hq, Hkv, D, dtype="bf16", grad=True)
+    kw = dict(softmax_scale=opt.get("scale", 0.11 if D == 128 else 0.15),
+              causal=opt.get("causal", False), window=opt.get("window", (-1, -1)),
+              softcap=opt.get("softcap", 0.0))
+    slopes = None
+    if opt.get("alibi"):
+        slopes = np.exp2(-8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+    dq, dk, dv = run_bwd_nd(b, w, {}, **kw)
+    rq, rk, rv = oracle_grads(w, kw, slopes)
+    check_o(to_f64(dq), rq, GRAD_ATOL, "dQ")
+    check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
+
+
+def test_bwd_nondeterministic_block_sparse(b):
+    w = inputs.random_case(77, 2, 300, 300, 4, 2, 128, dtype="bf16", grad=True, doc_len_range=(20, 90))
+    doc_t = torch.from_numpy(w["doc"]).cuda()
+    m = b.block_mask_build(2, 300, 300, 128, 128, causal=True, doc_q=doc_t, doc_k=doc_t)
+    dq, dk, dv = run_bwd_nd(b, w, {}, softmax_scale=0.12, block_mask=m)
+    rq, rk, rv = oracle.attention_bwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), f64(w, "do"), scale=0.12,
+                                      causal=True, doc_q=w["doc"], doc_k=w["doc"])
+    check_o(to_f64(dq), rq, GRAD_ATOL, "dQ")
+    check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
+
+
+def test_bwd_nondeterministic_llama8b_full(b):
+    """The B=1, Hq=32, Hkv=8, S=2048, D=128 causal workload with atomic dQ:
+    every gradient element against the oracle; dK and dV, which take no
+    atomics, are bitwise those of the deterministic schedule."""
+    w = inputs.llama8b_train()
+    kw = dict(softmax_scale=w["scale"], causal=True)
+    dq, dk, dv = run_bwd_nd(b, w, {}, **kw)
+    rq, rk, rv = oracle_grads(w, kw)
+    check_o(to_f64(dq), rq, GRAD_ATOL, "dQ")
+    check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
+    dq1, dk1, dv1 = run_bwd(b, w, **kw)
+    assert torch.equal(dk, dk1) and torch.equal(dv, dv1)
+    assert float((dq.float() - dq1.float()).abs().max()) <= 1e-2
