@@ -265,13 +265,15 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, window=(-1, -1),
 
 
 def decode(q, k_cache, v_cache, cache_seqlens, scale=None, softcap=0.0,
-           alibi_slopes=None, window=(-1, -1)):
+           alibi_slopes=None, window=(-1, -1), causal=False):
     """Attention of new queries over a KV cache ([FA] "Examples",
     ``flash_attn_with_kvcache``): q [B, Sq, Hq, D] attends to the first
     ``cache_seqlens[b]`` rows of k_cache/v_cache [B, Smax, Hkv, D] of its own
-    batch row.  The queries are the last Sq positions (bottom-right aligned),
-    so for Sq == 1 causal masking changes nothing.  This is the forward
-    definition with Sk = cache_seqlens[b]; it is computed unsplit.
+    batch row.  The queries are the last Sq positions (bottom-right aligned,
+    the forward's convention for Sq != Sk), so with ``causal`` query t sees the
+    first cache_seqlens[b] - Sq + 1 + t rows, and for Sq == 1 causal masking
+    changes nothing.  This is the forward definition with
+    Sk = cache_seqlens[b]; it is computed unsplit.
 
     Returns O [B, Sq, Hq, D] and LSE [B, Hq, Sq]."""
     B, Sq, Hq, D = q.shape
@@ -286,7 +288,7 @@ def decode(q, k_cache, v_cache, cache_seqlens, scale=None, softcap=0.0,
             slopes = np.asarray(slopes)[b:b + 1]
         o, l = attention_fwd(q[b:b + 1], k_cache[b:b + 1, :L],
                              v_cache[b:b + 1, :L], scale=scale,
-                             window=window, softcap=softcap,
+                             causal=causal, window=window, softcap=softcap,
                              alibi_slopes=slopes)
         O[b] = o[0]
         LSE[b] = l[0]

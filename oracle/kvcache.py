@@ -55,9 +55,12 @@ def kvcache_append(k_cache, v_cache, k_new, v_new, cache_seqlens, block_table=No
 
 
 def decode_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, page_size=None,
-                   cache_batch_idx=None, k_new=None, v_new=None, scale=None, softcap=0.0):
+                   cache_batch_idx=None, k_new=None, v_new=None, scale=None, softcap=0.0,
+                   causal=False):
     """Append (when k_new / v_new are given), then attend each sequence's
-    query to the first cache_seqlens[b] + S_new rows of its cache.
+    queries to the first cache_seqlens[b] + S_new rows of its cache (with
+    ``causal``, bottom-right aligned: the last query sees every row, query t
+    of Sq the first cache_seqlens[b] + S_new - Sq + 1 + t).
 
     Returns O [B, Sq, Hq, D], LSE [B, Hq, Sq] and the updated caches."""
     B = q.shape[0]
@@ -73,5 +76,5 @@ def decode_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, page_si
         n = int(lens[b])
         kc[b, :n] = cache_rows(k_cache, b, n, block_table, page_size, cache_batch_idx)
         vc[b, :n] = cache_rows(v_cache, b, n, block_table, page_size, cache_batch_idx)
-    O, L = decode(q, kc, vc, lens, scale=scale, softcap=softcap)
+    O, L = decode(q, kc, vc, lens, scale=scale, softcap=softcap, causal=causal)
     return O, L, (k_cache, v_cache)

@@ -638,3 +638,73 @@ def test_bf16_rounding_helpers():
     np.testing.assert_array_equal(back[:4], np.array([1.0, 1.0, 1.0078125, -2.5], dtype=np.float32))
     normal = np.abs(x) > 1e-37
     assert np.all(np.abs(back - x)[normal] <= np.abs(x)[normal] * 2.0 ** -8)
+
+
+# ---------------------------------------------------------------------------
+# several queries per sequence over a cache (chunked prefill, speculative
+# decoding): [FA] "Examples" lets q of flash_attn_with_kvcache hold seqlen
+# queries; with causal they are the last positions of the sequence.
+
+def test_decode_multi_query_causal_rows_are_single_token_decodes():
+    """[P22] Row t of a causal Sq-query decode over L keys equals the
+    single-query decode of q_t over the first L - Sq + 1 + t keys (its own
+    position); without causal every row sees all L keys.  Rows with no key
+    (L < Sq) give O = 0, LSE = -inf."""
+    rng = np.random.default_rng(31)
+    B, Sq, Hq, Hkv, D, Smax = 4, 5, 6, 2, 8, 40
+    q = rng.standard_normal((B, Sq, Hq, D))
+    kc, vc = rng.standard_normal((B, Smax, Hkv, D)), rng.standard_normal((B, Smax, Hkv, D))
+    lens = np.array([40, 5, 3, 17])
+    O, L = oracle.decode(q, kc, vc, lens, scale=0.3, softcap=2.0, causal=True)
+    On, Ln = oracle.decode(q, kc, vc, lens, scale=0.3, softcap=2.0)
+    for t in range(Sq):
+        own = np.maximum(lens - Sq + 1 + t, 0)
+        O1, L1 = oracle.decode(q[:, t:t + 1], kc, vc, own, scale=0.3, softcap=2.0)
+        np.testing.assert_allclose(O[:, t], O1[:, 0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L[:, :, t], L1[:, :, 0], rtol=0, atol=1e-13)
+        O2, L2 = oracle.decode(q[:, t:t + 1], kc, vc, lens, scale=0.3, softcap=2.0)
+        np.testing.assert_allclose(On[:, t], O2[:, 0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(Ln[:, :, t], L2[:, :, 0], rtol=0, atol=1e-13)
+    assert np.isneginf(L[2, :, :2]).all() and (O[2, :2] == 0).all()
+    assert np.isfinite(L[2, :, 2:]).all()
+
+
+def test_decode_multi_query_causal_brute_force():
+    """[P23] Causal multi-query decode against pure-Python loops with exact
+    sums (bottom-right causal predicate j <= i + L - Sq)."""
+    rng = np.random.default_rng(32)
+    B, Sq, Hq, Hkv, D, Smax = 2, 3, 4, 1, 5, 12
+    q = rng.standard_normal((B, Sq, Hq, D))
+    kc, vc = rng.standard_normal((B, Smax, Hkv, D)), rng.standard_normal((B, Smax, Hkv, D))
+    lens = np.array([12, 7])
+    O, L = oracle.decode(q, kc, vc, lens, scale=0.45, causal=True)
+    for b in range(B):
+        n = lens[b]
+        Ob, Lb = brute_fwd(q[b:b + 1], kc[b:b + 1, :n], vc[b:b + 1, :n], 0.45, causal=True)
+        np.testing.assert_allclose(O[b:b + 1], Ob, atol=1e-13)
+        np.testing.assert_allclose(L[b:b + 1], Lb, atol=1e-13)
+
+
+def test_decode_kvcache_speculative_append():
+    """[P24] Appending S_new draft tokens and attending them causally equals a
+    causal decode over the explicitly concatenated rows, and the last draft
+    row equals an ordinary one-token decode over all rows."""
+    rng = np.random.default_rng(33)
+    B, S_new, Hq, Hkv, D, Smax = 3, 4, 4, 2, 6, 32
+    q = rng.standard_normal((B, S_new, Hq, D))
+    kc, vc = rng.standard_normal((B, Smax, Hkv, D)), rng.standard_normal((B, Smax, Hkv, D))
+    kn, vn = rng.standard_normal((B, S_new, Hkv, D)), rng.standard_normal((B, S_new, Hkv, D))
+    lens = np.array([0, 9, 28])
+    O, L, _ = oracle.decode_kvcache(q, kc, vc, lens, k_new=kn, v_new=vn, scale=0.4, causal=True)
+    cat_k, cat_v = np.zeros_like(kc), np.zeros_like(vc)
+    for b in range(B):
+        n = lens[b]
+        cat_k[b, :n], cat_v[b, :n] = kc[b, :n], vc[b, :n]
+        cat_k[b, n:n + S_new], cat_v[b, n:n + S_new] = kn[b], vn[b]
+    for b in range(B):
+        n = lens[b] + S_new
+        Ob, Lb = brute_fwd(q[b:b + 1], cat_k[b:b + 1, :n], cat_v[b:b + 1, :n], 0.4, causal=True)
+        np.testing.assert_allclose(O[b:b + 1], Ob, atol=1e-13)
+        np.testing.assert_allclose(L[b:b + 1], Lb, atol=1e-13)
+    O1, L1 = oracle.decode(q[:, -1:], cat_k, cat_v, lens + S_new, scale=0.4)
+    np.testing.assert_allclose(O[:, -1], O1[:, 0], rtol=0, atol=1e-13)
