@@ -387,7 +387,54 @@ def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
         "ms_eager_launches": round(med, 5), "ms_eager_min": round(mn, 5),
         "hbm_gbs": round(algo_bytes / (gms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(algo_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del pcopies, o, ws
+
+    # speculative decoding on the same paged cache: 4 draft tokens per sequence
+    # (seeded normals, seed 63) are appended in place and attend causally,
+    # bottom-right aligned; Sq = 4, so 512 rows = 4 jobs per sequence
+    Sd = 4
+    rng = np.random.default_rng(63)
+    lens_d = torch.from_numpy(w["cache_seqlens"] - Sd).to(dev)
+    q4 = to_dev(inputs.f32_to_bf16_bits(rng.standard_normal((Bd, Sd, Hqd, Dd), dtype=np.float32)))
+    kn = to_dev(inputs.f32_to_bf16_bits(rng.standard_normal((Bd, Sd, 1, Dd), dtype=np.float32)))
+    vn = to_dev(inputs.f32_to_bf16_bits(rng.standard_normal((Bd, Sd, 1, Dd), dtype=np.float32)))
+    o4 = torch.empty_like(q4)
+    lse4 = torch.empty((Bd, Hqd, Sd), dtype=torch.float32, device=dev)
+
+    def spec_params(kk):
+        p = b._params(q4, kk, Dd, w["scale"], True, (-1, -1), None, 0.0, None)
+        p.Sk = w["block_table"].shape[1] * 256
+        kv = b.attn_kvcache()
+        kv.block_table = table.data_ptr()
+        kv.max_blocks = w["block_table"].shape[1]
+        kv.page_size = 256
+        kv.num_pages = kk.shape[0]
+        kv.k_new, kv.v_new, kv.s_new = b._tensor(kn), b._tensor(vn), Sd
+        return p, kv
+
+    p4, _ = spec_params(pcopies[0][1])
+    ws4 = torch.empty(lib.attn_decode_workspace_size(ctypes.byref(p4), 0), dtype=torch.uint8, device=dev)
+
+    def make_spec(st):
+        cs = []
+        for _, kk, vv in pcopies:
+            p, kv = spec_params(kk)
+            cs.append(Prepared(lib.attn_decode_kvcache,
+                               (ctypes.byref(p), b._tensor(q4), b._tensor(kk), b._tensor(vv),
+                                b._ptr(lens_d), ctypes.byref(kv), 0, b._tensor(o4), b._ptr(lse4),
+                                b._ptr(ws4), ws4.numel(), st)))
+            cs[-1].keep = (p, kv)
+        return cs, o4
+
+    gms, gsame = graph_timed(torch, np, make_spec)
+    seen = int(sum(Sd * int(n) - Sd * (Sd - 1) // 2 for n in w["cache_seqlens"]))
+    spec_bytes = total * Dd * 2 * 2 + 2 * Bd * Sd * Hqd * Dd * 2 + Bd * Hqd * Sd * 4 + 4 * Bd * Sd * Dd * 2
+    ex["specdecode_mqa_b32_h128_q4_paged256"] = {
+        "ms": round(gms, 5), "graph_replay_matches_eager": gsame,
+        "hbm_gbs": round(spec_bytes / (gms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(spec_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "tflops": round(4.0 * Hqd * Dd * seen / (gms * 1e-3) / 1e12, 2),
+        "algorithmic_bytes": spec_bytes}
+    del pcopies, o, ws, q4, kn, vn, o4, ws4
 
     # long-context local attention: S=16384, causal + window (4096, 0)
     w = inputs.long_local()

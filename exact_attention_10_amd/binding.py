@@ -295,15 +295,16 @@ def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softma
 
 def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=0.0,
                 num_splits=0, out=None, lse=None, workspace=None, block_table=None,
-                cache_batch_idx=None, k_new=None, v_new=None):
-    """Decode over a KV cache.  q [B, 1, Hq, D]; caches [B, Smax, Hkv, D]
+                cache_batch_idx=None, k_new=None, v_new=None, causal=False):
+    """Decode over a KV cache.  q [B, Sq, Hq, D] (the last Sq positions of
+    each sequence; causal: bottom-right aligned); caches [B, Smax, Hkv, D]
     (paged: [num_pages, page_size, Hkv, D] with block_table int32
     [B, max_blocks]); cache_seqlens int32 [B] on the device; optional
     cache_batch_idx int32 [B] (contiguous caches) and k_new / v_new
     [B, s_new, Hkv, D] appended in place at rows [L_b, L_b + s_new).
-    Returns (out, lse [B, Hq, 1])."""
+    Returns (out, lse [B, Hq, Sq])."""
     B, Sq, Hq, D = q.shape
-    p = _params(q, k_cache, D, softmax_scale, False, (-1, -1), None, softcap, None)
+    p = _params(q, k_cache, D, softmax_scale, causal, (-1, -1), None, softcap, None)
     kv = None
     if block_table is not None or cache_batch_idx is not None or k_new is not None:
         kv = attn_kvcache()
@@ -346,8 +347,8 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
     return out, lse
 
 
-def decode_workspace_size(q, k_cache, num_splits=0, softcap=0.0):
-    p = _params(q, k_cache, q.shape[3], None, False, (-1, -1), None, softcap, None)
+def decode_workspace_size(q, k_cache, num_splits=0, softcap=0.0, causal=False):
+    p = _params(q, k_cache, q.shape[3], None, causal, (-1, -1), None, softcap, None)
     return _lib.attn_decode_workspace_size(ctypes.byref(p), int(num_splits))
 
 

@@ -336,7 +336,7 @@ size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits) {
   if (p == nullptr || p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->D <= 0 || p->Sk <= 0 ||
       num_splits < 0 || num_splits > 65536)
     return 0;
-  return attn::decode_workspace(p->B, p->Hq, p->Hkv, p->D, attn::decode_parts(num_splits)).bytes;
+  return attn::decode_workspace(p->B, p->Hq, p->Hkv, p->Sq, p->D, attn::decode_parts(num_splits)).bytes;
 }
 
 static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor k_cache,
@@ -347,10 +347,11 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
   Common cm;
   attn_status st = check_params(p, &cm);
   if (st != ATTN_OK) return st;
-  if (p->Sq != 1) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode takes one query per sequence (Sq=%d)", p->Sq);
-  if (p->causal || p->window_left != -1 || p->window_right != -1 || p->alibi_slopes != nullptr ||
-      p->block_mask != nullptr)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports scale and softcap only");
+  if (p->Sq < 1 || p->Sq > p->Sk)
+    return fail(ATTN_ERR_INVALID_ARG, "attn_decode takes 1 <= Sq <= Sk queries per sequence (Sq=%d, Sk=%d)",
+                p->Sq, p->Sk);
+  if (p->window_left != -1 || p->window_right != -1 || p->alibi_slopes != nullptr || p->block_mask != nullptr)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports scale, softcap and causal only");
   const int32_t dt = q.dtype;
   if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports bf16 only");
   const bool paged = kv != nullptr && kv->block_table != nullptr;
@@ -373,7 +374,7 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
     return fail(ATTN_ERR_INVALID_ARG, "cache_batch must be positive with cache_batch_idx");
   if (append && (kv->s_new <= 0 || kv->s_new > p->Sk))
     return fail(ATTN_ERR_INVALID_ARG, "s_new must be in [1, Sk] (got %d)", kv->s_new);
-  if ((st = check_tensor("q", q, dt, p->B, 1, p->Hq, true)) != ATTN_OK) return st;
+  if ((st = check_tensor("q", q, dt, p->B, p->Sq, p->Hq, true)) != ATTN_OK) return st;
   const int64_t cache_rows0 = paged ? kv->num_pages : (remap ? kv->cache_batch : p->B);
   const int64_t cache_rows1 = paged ? kv->page_size : p->Sk;
   if ((st = check_tensor("k_cache", k_cache, dt, cache_rows0, cache_rows1, p->Hkv, true)) != ATTN_OK) return st;
@@ -382,7 +383,7 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
     if ((st = check_tensor("k_new", kv->k_new, dt, p->B, kv->s_new, p->Hkv, true)) != ATTN_OK) return st;
     if ((st = check_tensor("v_new", kv->v_new, dt, p->B, kv->s_new, p->Hkv, true)) != ATTN_OK) return st;
   }
-  if ((st = check_tensor("o", o, dt, p->B, 1, p->Hq, true)) != ATTN_OK) return st;
+  if ((st = check_tensor("o", o, dt, p->B, p->Sq, p->Hq, true)) != ATTN_OK) return st;
   if (p->B > 0 && (cache_seqlens == nullptr || lse == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "cache_seqlens and lse must not be NULL");
   if (num_splits < 0 || num_splits > 65536)
@@ -398,11 +399,13 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
   a.q = q.data; a.k = k_cache.data; a.v = v_cache.data; a.o = o.data;
   a.lse = lse;
   a.seqlens = cache_seqlens;
-  a.q_sb = q.stride[0]; a.q_sh = q.stride[2];
+  a.q_sb = q.stride[0]; a.q_ss = q.stride[1]; a.q_sh = q.stride[2];
   strides3(k_cache, &a.k_sb, &a.k_ss, &a.k_sh);
   strides3(v_cache, &a.v_sb, &a.v_ss, &a.v_sh);
-  a.o_sb = o.stride[0]; a.o_sh = o.stride[2];
+  a.o_sb = o.stride[0]; a.o_ss = o.stride[1]; a.o_sh = o.stride[2];
   a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.D = p->D; a.Smax = p->Sk;
+  a.Sq = p->Sq;
+  a.causal = p->causal ? 1 : 0;
   a.scale = cm.scale;
   a.softcap = p->softcap;
   if (paged) {
@@ -425,8 +428,8 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
     strides3(kv->v_new, &a.vn_sb, &a.vn_ss, &a.vn_sh);
   }
   a.parts = attn::decode_parts(num_splits);
-  a.nhg = attn::decode_head_groups(p->Hq, p->Hkv);
-  const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->D, a.parts);
+  a.nhg = attn::decode_head_groups(p->Hq, p->Hkv, p->Sq);
+  const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->Sq, p->D, a.parts);
   char* wsb = static_cast<char*>(workspace);
   a.part_o = reinterpret_cast<float*>(wsb + wl.o_off);
   a.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);

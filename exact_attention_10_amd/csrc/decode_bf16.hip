@@ -1,15 +1,21 @@
 // Split-K decode over a KV cache, bf16 (gfx950).
 //
 // flash_attn_with_kvcache ("FlashAttention: Fast and Memory-Efficient Exact
-// Attention", "Examples") attends one new query per sequence to the first
-// cache_seqlens[b] rows of that sequence's cache.  The key work is split and
+// Attention", "Examples") attends the new queries of each sequence (one, or a
+// few for chunked prefill and speculative decoding) to the first
+// cache_seqlens[b] rows of that sequence's cache; with several queries they
+// are the last positions of the sequence, so causal masking (bottom-right
+// aligned) limits query t of Sq to the first L - Sq + 1 + t keys.  The key
+// work is split and
 // merged with the LSE-weighted combine
 //   lse = log sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) O_s
 // (the chunk-level form of the online softmax of "Accelerating AI: A Deep
 // Dive into Flash Attention", "2. Online Softmax").
 //
 // Work decomposition.  A job is one (sequence b, kv head, group of up to 128
-// query heads of that kv head); its keys are cut into 32-key steps.  All
+// rows of that kv head), a row being a (query t, query head) pair numbered
+// t * G + head (G query heads per kv head); its keys are cut into 32-key
+// steps.  All
 // jobs' steps, in job order, form one list of S steps that is cut into
 // Pe = min(P, S) equal contiguous ranges, one per workgroup (P = one per
 // compute unit by default), so every workgroup streams the same number of K/V
@@ -172,7 +178,7 @@ struct Cursor {
   int left;                       // K/V steps left in this workgroup's range
 };
 
-template <int D, bool kSoftcap>
+template <int D, bool kSoftcap, bool kMulti>
 __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeArgs a) {
   using C = DecCfg<D>;
   using L = typename C::L;
@@ -191,6 +197,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   const int hb = wave & 3, par = (wave >> 2) & 1;  // consumer head block and step parity
   const int g = lane >> 5, c = lane & 31;
   const int G = a.Hq / a.Hkv;
+  const int R = a.Sq * G;         // rows per kv head
   const int jpb = a.Hkv * a.nhg;  // jobs per sequence
   const int P = gridDim.x;
   const int w_id = blockIdx.x;
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   auto set_job = [&](Cursor& cu) {
     cu.g_kv = cu.jb / a.nhg;
     cu.hg = cu.jb - cu.g_kv * a.nhg;
-    cu.rows = min(C::ROWS, G - cu.hg * C::ROWS);
+    cu.rows = min(C::ROWS, R - cu.hg * C::ROWS);
     cu.nq = cu.rows > 64 ? 2 : 1;
   };
   auto start = [&](Cursor& cu) {
@@ -317,15 +324,16 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     // registers in the consumer waves.)
     const int lrow = lane % L::RG, cp_chunk = lane / L::RG;
     char* item = ring + slot * C::SB;
-    if (pc.phase < pc.nq) {  // query heads [64 phase, 64 phase + 64) of the job
-      const char* qb = static_cast<const char*>(a.q) +
-                       ((int64_t)pc.b * a.q_sb + (int64_t)(pc.g_kv * G + pc.hg * C::ROWS) * a.q_sh) * 2;
+    if (pc.phase < pc.nq) {  // rows [64 phase, 64 phase + 64) of the job
+      const char* qb = static_cast<const char*>(a.q) + ((int64_t)pc.b * a.q_sb + (int64_t)pc.g_kv * G * a.q_sh) * 2;
 #pragma unroll
       for (int u = 0; u < C::PER; ++u) {
         const int cpy = pw + C::NWP * u, mat = cpy / C::GROUPS, grp = cpy % C::GROUPS;
         int r = 64 * pc.phase + 32 * mat + grp * L::RG + lrow;
-        r = r < pc.rows ? r : pc.rows - 1;  // heads past the job's last repeat it (unused)
-        dma16(qb + ((int64_t)r * a.q_sh + cp_chunk * 8) * 2, lds_addr(item + mat * C::TB + grp * L::GS));
+        r = pc.hg * C::ROWS + (r < pc.rows ? r : pc.rows - 1);  // rows past the job's last repeat it (unused)
+        const int t = kMulti || a.Sq > 1 ? r / G : 0;
+        const int64_t roff = (int64_t)t * a.q_ss + (int64_t)(r - t * G) * a.q_sh;
+        dma16(qb + (roff + cp_chunk * 8) * 2, lds_addr(item + mat * C::TB + grp * L::GS));
       }
     } else {
       const int row0 = pc.step * C::BN;
@@ -387,6 +395,9 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 
   bf16x8 qf[C::DSTEPS];
   float m_run = kNegInf, l_run = 0.0f;  // m_run in exp2 units
+  // kMulti (causal, several queries): keys this lane's row may see, and the
+  // smallest such count in the wave (steps below it need no mask).
+  int lim_row = 0, lim_wave = 0;
   f32x16 oacc[C::DBLK];
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) qf[ds] = bf16x8{};
@@ -428,6 +439,19 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
           sacc[t][r] = cap_log2 * (1.0f - 2.0f * fast_rcp(e + 1.0f));
         }
     }
+    // Causal rows: keys at or past the row's own count are real keys of later
+    // positions, so they are removed before the max.
+    if constexpr (kMulti) {
+#pragma unroll
+      for (int t = 0; t < NI; ++t) {
+        if ((step + t + 1) * C::BN > lim_wave) {
+          const int key0 = (step + t) * C::BN + 4 * g;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[t][r] = key0 + 8 * (r >> 2) + (r & 3) < lim_row ? sacc[t][r] : kNegInf;
+        }
+      }
+    }
     // (Plain fmaxf here: the matrix-core results must be read by compiled
     // instructions, which get the MFMA -> VALU wait states.)
     float mt[NI];
@@ -454,13 +478,16 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     }
     bf16x8 pf[NI][2];
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // (A row with no visible key yet keeps m_run = -inf; all its scores are
+    // -inf then, and a zero reference keeps exp2 at 0 instead of NaN.)
+    const float m_use = kMulti && m_run == kNegInf ? 0.0f : m_run;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        p[r] = kSoftcap ? fast_exp2(sacc[t][r] - m_run) : fast_exp2(__builtin_fmaf(sacc[t][r], scl, -m_run));
-      if ((step + t + 1) * C::BN > Lb) {
+        p[r] = kSoftcap ? fast_exp2(sacc[t][r] - m_use) : fast_exp2(__builtin_fmaf(sacc[t][r], scl, -m_use));
+      if (!kMulti && (step + t + 1) * C::BN > Lb) {
         const int key0 = (step + t) * C::BN + 4 * g;
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = key0 + 8 * (r >> 2) + (r & 3) < Lb ? p[r] : 0.0f;
@@ -612,6 +639,11 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+      if constexpr (kMulti) {
+        const int r0 = cc.hg * C::ROWS + hb * 32;
+        lim_row = cc.Lb - a.Sq + 1 + min(r0 + c, R - 1) / G;
+        lim_wave = cc.Lb - a.Sq + 1 + r0 / G;
+      }
       if (hb * 32 < cc.rows) {
         const char* qt = ring + ((i + (hb >> 1)) % C::NS) * C::SB + (hb & 1) * C::TB;
 #pragma unroll
@@ -654,11 +686,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int b = j / jpb, jb = j % jpb;
   const int g_kv = jb / a.nhg, hg = jb % a.nhg;
   const int G = a.Hq / a.Hkv;
-  const int rows = min(ROWS, G - hg * ROWS);
+  const int rows = min(ROWS, a.Sq * G - hg * ROWS);
   const int r = blockIdx.y * HPB + threadIdx.x / TPH;
   if (r >= rows) return;
   const int d4 = threadIdx.x % TPH;
-  const int h = g_kv * G + hg * ROWS + r;
+  const int jr = hg * ROWS + r;  // row = query t * G + head
+  const int t = jr / G;
+  const int h = g_kv * G + (jr - t * G);
   const int Lb = seq_len(a, b);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float m = kNegInf, tot = 0.0f;
@@ -700,13 +734,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     }
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-  bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)h * a.o_sh + 4 * d4;
+  bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)t * a.o_ss + (int64_t)h * a.o_sh + 4 * d4;
   const uint32_t lo2 = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.x * inv)) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.y * inv)) << 16);
   const uint32_t hi2 = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.z * inv)) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.w * inv)) << 16);
   *reinterpret_cast<uint2*>(op) = make_uint2(lo2, hi2);
-  if (d4 == 0) a.lse[(int64_t)b * a.Hq + h] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
+  if (d4 == 0) a.lse[((int64_t)b * a.Hq + h) * a.Sq + t] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
 }
 
 // In-place append: rows [L_b, L_b + len_add) of sequence b's cache (paged or
@@ -752,8 +786,14 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const dim3 block(DecCfg<D>::NT);
-  if (a.softcap > 0.0f) hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(a.parts), block, 0, s, a);
-  else hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(a.parts), block, 0, s, a);
+  const bool multi = a.causal && a.Sq > 1;
+  if (a.softcap > 0.0f) {
+    if (multi) hipLaunchKernelGGL((decode_split_kernel<D, true, true>), dim3(a.parts), block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, true, false>), dim3(a.parts), block, 0, s, a);
+  } else {
+    if (multi) hipLaunchKernelGGL((decode_split_kernel<D, false, true>), dim3(a.parts), block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, false, false>), dim3(a.parts), block, 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int HPB = 256 / (D / 4);
@@ -765,7 +805,9 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int decode_head_groups(int Hq, int Hkv) { return (Hq / Hkv + kDecodeRows - 1) / kDecodeRows; }
+int decode_head_groups(int Hq, int Hkv, int Sq) {
+  return (int)(((int64_t)Sq * (Hq / Hkv) + kDecodeRows - 1) / kDecodeRows);
+}
 
 int decode_parts(int num_splits) {
   if (num_splits > 0) return num_splits;
@@ -781,9 +823,9 @@ int decode_parts(int num_splits) {
   return cus[dev];
 }
 
-DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int D, int parts) {
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int parts) {
   DecodeWorkspace w;
-  const size_t jobs = (size_t)B * Hkv * decode_head_groups(Hq, Hkv);
+  const size_t jobs = (size_t)B * Hkv * decode_head_groups(Hq, Hkv, Sq);
   const size_t slots = (size_t)parts + jobs;
   w.o_off = 0;
   w.lse_off = (slots * kDecodeRows * D * sizeof(float) + 255) / 256 * 256;

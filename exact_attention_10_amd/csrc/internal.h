@@ -100,17 +100,22 @@ struct DecodeArgs {
   const void* q; const void* k; const void* v; void* o;
   float* lse;
   const int32_t* seqlens;
-  int64_t q_sb, q_sh;
+  int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
-  int64_t o_sb, o_sh;
+  int64_t o_sb, o_ss, o_sh;
   int B, Hq, Hkv, D, Smax;
+  // Sq queries per sequence, the last Sq positions of it; a job's rows are
+  // (query t, head) pairs, row = t * (Hq / Hkv) + head within the kv head.
+  // causal: query t sees the first L - Sq + 1 + t keys (L keys in all).
+  int Sq, causal;
   float scale;
   float softcap;
   int parts;                 // workgroups; the key work is cut into this many equal ranges
   int nhg;                   // groups of up to kDecodeRows query heads per kv head
   float* part_o;             // workspace [parts + jobs][kDecodeRows][D]
   float* part_lse;           // workspace [parts + jobs][kDecodeRows]
+                             // (a job: sequence, kv head, up to kDecodeRows rows)
   int32_t* job_seg;          // workspace [jobs][2]: first and last workgroup of each job
   // KV-cache addressing.  Contiguous: sequence b uses batch row batch_idx[b]
   // (b when null) of k/v.  Paged (block_table != null): row r of sequence b is
@@ -126,14 +131,14 @@ struct DecodeArgs {
   const void* k_new; const void* v_new;
   int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;
 };
-constexpr int kDecodeRows = 128;  // query heads per decode job
+constexpr int kDecodeRows = 128;  // rows (query, head) per decode job
 // Number of workgroups: num_splits when > 0, else the device's compute units.
 int decode_parts(int num_splits);
-int decode_head_groups(int Hq, int Hkv);
+int decode_head_groups(int Hq, int Hkv, int Sq);  // jobs per (sequence, kv head)
 struct DecodeWorkspace {
   size_t o_off, lse_off, seg_off, bytes;
 };
-DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int D, int parts);
+DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int parts);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
 struct BlockMaskArgs {

@@ -235,22 +235,29 @@ attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
 /* ---------------------------------------------------------------------
  * Decode over a KV cache ([FA] flash_attn_with_kvcache: q attends to the
  * first cache_seqlens[b] rows of its batch row of k_cache / v_cache; no
- * backward).  Split-K: the keys of every (sequence, kv head, group of up to
- * 128 query heads) job, in 32-key steps and job order, are cut into equal
+ * backward).  The Sq queries of a sequence are its last Sq positions (one
+ * token, or a chunk of a prefill, or the draft tokens of speculative
+ * decoding); with p->causal, bottom-right aligned as in attn_fwd, query t
+ * attends to the first L - Sq + 1 + t of its L keys (none if that is <= 0:
+ * o = 0, lse = -inf).  Split-K: the keys of every job (sequence, kv head,
+ * group of up to 128 rows, a row being a (query t, query head) pair numbered
+ * t * (Hq/Hkv) + head), in 32-key steps and job order, are cut into equal
  * contiguous ranges, one per workgroup; the pieces are attended
  * independently and merged with the LSE-weighted combine
- * lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.
- *   p : B, Sq (== 1), Hq, Hkv, D as usual; Sk = cache capacity Smax;
- *       scale and softcap apply; causal, window, ALiBi and block masks are
- *       not supported by this entry point (UNSUPPORTED).
- *   q : [B, 1, Hq, D];  k_cache, v_cache : [B, Smax, Hkv, D].
+ * lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s.  Each job
+ * reads its sequence's keys once, so Sq * Hq/Hkv <= 128 reads them once.
+ *   p : B, Sq (1 <= Sq <= Sk, else INVALID_ARG), Hq, Hkv, D as usual;
+ *       Sk = cache capacity Smax; scale, softcap and causal apply; window,
+ *       ALiBi and block masks are not supported by this entry point
+ *       (UNSUPPORTED).
+ *   q : [B, Sq, Hq, D];  k_cache, v_cache : [B, Smax, Hkv, D].
  *   cache_seqlens : device int32 [B], each in [0, Smax] (values outside are
  *       clamped to that range on the device).  A sequence of length 0 gives
  *       o = 0 and lse = -inf.
  *   num_splits : number of ranges (workgroups) the total key work is cut
  *       into; 0 = one per compute unit of the current device.  At most
  *       65536.  Any value gives the same result up to rounding.
- *   o : [B, 1, Hq, D];  lse : fp32 [B, Hq, 1] contiguous.
+ *   o : [B, Sq, Hq, D];  lse : fp32 [B, Hq, Sq] contiguous.
  *   workspace : at least attn_decode_workspace_size(p, num_splits) bytes.
  */
 attn_status attn_decode(const attn_params* p, attn_tensor q,
@@ -277,7 +284,8 @@ size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits);
  *   k_new, v_new : [B, s_new, Hkv, D] bf16 (data NULL = no append).  Before
  *       attending, rows [L_b, L_b + s_new) of each sequence's cache receive
  *       them (L_b = cache_seqlens[b], clamped to [0, Sk - s_new]) and the
- *       query then attends to L_b + s_new rows.  cache_seqlens is read, not
+ *       queries then attend to L_b + s_new rows (with causal and
+ *       Sq == s_new, query t sees the cache and the new rows up to t).  cache_seqlens is read, not
  *       advanced.  The caches are written in place (stream-ordered).
  * Other arguments, outputs, workspace and errors as attn_decode (which is
  * this call with a NULL kv).  Errors: INVALID_ARG for a page_size that is
