@@ -147,13 +147,22 @@ def test_decode_validation(b):
     assert need > 0
     st = lib.attn_decode(ctypes.byref(p), q, kc, kc, FAKE, 0, q, FAKE, None, 0, None)
     assert st == 3
-    p2 = params(b, B=4, Sq=2, Sk=1024, Hq=8, Hkv=1, D=128)
-    st = lib.attn_decode(ctypes.byref(p2), tensor(b, (4, 2, 8, 128)), kc, kc, FAKE, 0,
-                         tensor(b, (4, 2, 8, 128)), FAKE, FAKE, need, None)
-    assert st == 2
+    # more queries than cache rows
+    p2 = params(b, B=4, Sq=1025, Sk=1024, Hq=8, Hkv=1, D=128)
+    st = lib.attn_decode(ctypes.byref(p2), tensor(b, (4, 1025, 8, 128)), kc, kc, FAKE, 0,
+                         tensor(b, (4, 1025, 8, 128)), FAKE, FAKE, need, None)
+    assert st == 1 and b"Sq" in lib.attn_last_error()
+    # a window is not a decode option (causal is)
     p3 = params(b, B=4, Sq=1, Sk=1024, Hq=8, Hkv=1, D=128, causal=1)
+    p3.window_left = 16
     st = lib.attn_decode(ctypes.byref(p3), q, kc, kc, FAKE, 0, q, FAKE, FAKE, need, None)
     assert st == 2
+    p4 = params(b, B=4, Sq=3, Sk=1024, Hq=8, Hkv=1, D=128, causal=1)
+    # 3 queries x 8 heads = 24 rows per kv head: still one job per sequence;
+    # 48 queries x 8 heads need 3 jobs and more workspace
+    assert lib.attn_decode_workspace_size(ctypes.byref(p4), 0) == need
+    p5 = params(b, B=4, Sq=48, Sk=1024, Hq=8, Hkv=1, D=128, causal=1)
+    assert lib.attn_decode_workspace_size(ctypes.byref(p5), 0) > need
     st = lib.attn_decode(ctypes.byref(p), q, kc, kc, None, 0, q, FAKE, FAKE, need, None)
     assert st == 1
     # more splits need at least as much workspace
