@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 ATTN_OK = 0
 ATTN_BF16 = 0
 ATTN_FP32 = 1
+ATTN_FP16 = 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
           3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
 
@@ -140,9 +141,11 @@ def _check(status):
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_FP16
     if t.dtype == torch.float32:
         return ATTN_FP32
-    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+    raise TypeError("unsupported dtype %s (bfloat16, float16 or float32)" % t.dtype)
 
 
 def _tensor(t):
@@ -280,6 +283,52 @@ def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, window=(
                          1 if deterministic else 0, _ptr(workspace), workspace.numel(),
                          _stream()))
     return dq, dk, dv
+
+
+def _unpack(x, n, name):
+    if x.dim() != 5 or x.shape[2] != n:
+        raise ValueError("%s must be [B, S, %d, H, D], got shape %s" % (name, n, tuple(x.shape)))
+    return [x[:, :, i] for i in range(n)]
+
+
+def attn_fwd_qkvpacked(qkv, softmax_scale=None, causal=False, window=(-1, -1), alibi_slopes=None,
+                       softcap=0.0, out=None, lse=None):
+    """Forward on a packed qkv [B, S, 3, H, D] ([FA] flash_attn_qkvpacked_func):
+    q, k, v are strided views of it, no copy.  Returns (out, lse)."""
+    q, k, v = _unpack(qkv, 3, "qkv")
+    return attn_fwd(q, k, v, softmax_scale, causal, window, alibi_slopes, softcap, out=out, lse=lse)
+
+
+def attn_bwd_qkvpacked(qkv, out, dout, lse, softmax_scale=None, causal=False, window=(-1, -1),
+                       alibi_slopes=None, softcap=0.0, deterministic=True, dqkv=None, workspace=None):
+    """Backward of attn_fwd_qkvpacked with the gradient in the packed layout:
+    dq, dk, dv are written straight into views of one dqkv [B, S, 3, H, D]."""
+    q, k, v = _unpack(qkv, 3, "qkv")
+    dqkv = torch.empty_like(qkv) if dqkv is None else dqkv
+    dq, dk, dv = _unpack(dqkv, 3, "dqkv")
+    attn_bwd(q, k, v, out, dout, lse, softmax_scale, causal, window, alibi_slopes, softcap,
+             deterministic, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    return dqkv
+
+
+def attn_fwd_kvpacked(q, kv, softmax_scale=None, causal=False, window=(-1, -1), alibi_slopes=None,
+                      softcap=0.0, out=None, lse=None):
+    """Forward with a packed kv [B, Sk, 2, Hkv, D] ([FA] flash_attn_kvpacked_func)."""
+    k, v = _unpack(kv, 2, "kv")
+    return attn_fwd(q, k, v, softmax_scale, causal, window, alibi_slopes, softcap, out=out, lse=lse)
+
+
+def attn_bwd_kvpacked(q, kv, out, dout, lse, softmax_scale=None, causal=False, window=(-1, -1),
+                      alibi_slopes=None, softcap=0.0, deterministic=True, dq=None, dkv=None,
+                      workspace=None):
+    """Backward of attn_fwd_kvpacked; returns (dq, dkv) with dkv [B, Sk, 2, Hkv, D]."""
+    k, v = _unpack(kv, 2, "kv")
+    dkv = torch.empty_like(kv) if dkv is None else dkv
+    dk, dv = _unpack(dkv, 2, "dkv")
+    dq = torch.empty_like(q) if dq is None else dq
+    attn_bwd(q, k, v, out, dout, lse, softmax_scale, causal, window, alibi_slopes, softcap,
+             deterministic, dq=dq, dk=dk, dv=dv, workspace=workspace)
+    return dq, dkv
 
 
 def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softmax_scale=None,

@@ -120,13 +120,13 @@ attn_status check_block_mask(const attn_params* p, int32_t dtype) {
     return fail(ATTN_ERR_INVALID_ARG, "block mask lists are NULL");
   if ((bm->desc.doc_q == nullptr) != (bm->desc.doc_k == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "block mask: give both doc_q and doc_k or neither");
-  const int bn_kernel = dtype == ATTN_BF16 ? attn::kFwdBN : attn::kFwdF32BN;
-  const int bm_kernel = dtype == ATTN_BF16 ? attn::kFwdBM : attn::kFwdF32BM;
-  const bool m_ok = dtype == ATTN_BF16 ? bm->block_m == bm_kernel : bm->block_m % bm_kernel == 0;
+  const int bn_kernel = dtype != ATTN_FP32 ? attn::kFwdBN : attn::kFwdF32BN;
+  const int bm_kernel = dtype != ATTN_FP32 ? attn::kFwdBM : attn::kFwdF32BM;
+  const bool m_ok = dtype != ATTN_FP32 ? bm->block_m == bm_kernel : bm->block_m % bm_kernel == 0;
   if (!m_ok || bm->block_n <= 0 || bm->block_n % bn_kernel != 0)
     return fail(ATTN_ERR_UNSUPPORTED,
                 "block mask tile %dx%d is not supported (rows %s %d, columns a multiple of %d)",
-                bm->block_m, bm->block_n, dtype == ATTN_BF16 ? "==" : "a multiple of", bm_kernel,
+                bm->block_m, bm->block_n, dtype != ATTN_FP32 ? "==" : "a multiple of", bm_kernel,
                 bn_kernel);
   if (bm->nQ != (p->Sq + bm->block_m - 1) / bm->block_m || bm->nK != (p->Sk + bm->block_n - 1) / bm->block_n)
     return fail(ATTN_ERR_INVALID_ARG, "block mask tile grid does not match its sizes");
@@ -155,11 +155,12 @@ attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype, int32_t* bl
   g_err[0] = 0;
   if (p == nullptr || block_m == nullptr || block_n == nullptr)
     return fail(ATTN_ERR_INVALID_ARG, "NULL argument");
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16 && dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (p->block_mask != nullptr) {
     *block_m = p->block_mask->block_m;
     *block_n = p->block_mask->block_n;
-  } else if (dtype == ATTN_BF16) {
+  } else if (dtype != ATTN_FP32) {
     *block_m = attn::fwd_bf16_rows_per_block(p->B, p->Sq, p->Hq, p->causal, false);
     *block_n = attn::kFwdBN;
   } else {
@@ -179,7 +180,7 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
   attn_status st = check_params(p, &cm);
   if (st != ATTN_OK) return st;
   const int32_t dt = q.dtype;
-  if (dt != ATTN_BF16 && dt != ATTN_FP32) return fail(ATTN_ERR_UNSUPPORTED, "q: dtype %d", dt);
+  if (dt != ATTN_BF16 && dt != ATTN_FP16 && dt != ATTN_FP32) return fail(ATTN_ERR_UNSUPPORTED, "q: dtype %d", dt);
   if ((st = check_tensor("q", q, dt, p->B, p->Sq, p->Hq, true)) != ATTN_OK) return st;
   if ((st = check_tensor("k", k, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
   if ((st = check_tensor("v", v, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
@@ -189,6 +190,7 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
 
   attn::FwdArgs a{};
   a.q = q.data; a.k = k.data; a.v = v.data; a.o = o.data;
+  a.f16 = dt == ATTN_FP16;
   a.lse = lse;
   a.trace = tile_trace;
   strides3(q, &a.q_sb, &a.q_ss, &a.q_sh);
@@ -210,18 +212,18 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
     a.tiles.nQ = bm->nQ;
     a.tiles.nK = bm->nK;
     a.tiles.block_m = bm->block_m;
-    a.tiles.sub = bm->block_n / (dt == ATTN_BF16 ? attn::kFwdBN : attn::kFwdF32BN);
+    a.tiles.sub = bm->block_n / (dt != ATTN_FP32 ? attn::kFwdBN : attn::kFwdF32BN);
     a.nQt = bm->nQ;
     a.nKt = bm->nK;
   } else {
-    const int bmr = dt == ATTN_BF16 ? attn::fwd_bf16_rows_per_block(p->B, p->Sq, p->Hq, p->causal, false)
+    const int bmr = dt != ATTN_FP32 ? attn::fwd_bf16_rows_per_block(p->B, p->Sq, p->Hq, p->causal, false)
                                     : attn::kFwdF32BM;
-    const int bnr = dt == ATTN_BF16 ? attn::kFwdBN : attn::kFwdF32BN;
+    const int bnr = dt != ATTN_FP32 ? attn::kFwdBN : attn::kFwdF32BN;
     a.nQt = (p->Sq + bmr - 1) / bmr;
     a.nKt = (p->Sk + bnr - 1) / bnr;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dt == ATTN_BF16 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s);
+  hipError_t e = dt != ATTN_FP32 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s);
   return hip_status(e, "attn_fwd launch");
 }
 
@@ -234,7 +236,8 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
   attn_status st = check_params(p, &cm);
   if (st != ATTN_OK) return st;
   const int32_t dt = q.dtype;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd supports bf16 only");
+  if (dt != ATTN_BF16 && dt != ATTN_FP16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd supports bf16 and fp16 (dtype %d)", dt);
   if ((st = check_tensor("q", q, dt, p->B, p->Sq, p->Hq, true)) != ATTN_OK) return st;
   if ((st = check_tensor("k", k, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
   if ((st = check_tensor("v", v, dt, p->B, p->Sk, p->Hkv, true)) != ATTN_OK) return st;
@@ -263,6 +266,7 @@ static attn_status bwd_impl(const attn_params* p, attn_tensor q, attn_tensor k, 
     return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   attn::BwdArgs a{};
+  a.f16 = dt == ATTN_FP16;
   a.q = q.data; a.k = k.data; a.v = v.data; a.o = o.data; a.dout = dout.data;
   a.lse = lse;
   a.dq = dq.data; a.dk = dk.data; a.dv = dv.data;
@@ -353,7 +357,8 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
   if (p->window_left != -1 || p->window_right != -1 || p->alibi_slopes != nullptr || p->block_mask != nullptr)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports scale, softcap and causal only");
   const int32_t dt = q.dtype;
-  if (dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports bf16 only");
+  if (dt != ATTN_BF16 && dt != ATTN_FP16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_decode supports bf16 and fp16 (dtype %d)", dt);
   const bool paged = kv != nullptr && kv->block_table != nullptr;
   const bool remap = kv != nullptr && kv->cache_batch_idx != nullptr;
   const bool append = kv != nullptr && kv->k_new.data != nullptr;
@@ -396,6 +401,7 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
     return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   attn::DecodeArgs a{};
+  a.f16 = dt == ATTN_FP16;
   a.q = q.data; a.k = k_cache.data; a.v = v_cache.data; a.o = o.data;
   a.lse = lse;
   a.seqlens = cache_seqlens;

@@ -1,4 +1,4 @@
-// Backward attention from the saved log-sum-exp, bf16 (gfx950).
+// Backward attention from the saved log-sum-exp, bf16 or fp16 (gfx950).
 //
 // "Lightning Talk: FlexAttention + FlashAttention-4" notes that the backward
 // reuses the forward's machinery; "FlashAttention: Fast and Memory-Efficient
@@ -43,7 +43,7 @@ constexpr float kPosInf = __builtin_huge_valf();
 // 1. Delta = rowsum(dO * O), one 16-lane group per (b, i, h) row; the same
 //    pass stores the LSE in exp2 units for the dK/dV kernel.
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;  // lanes per row (8 elements each)
   const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
     const uint32_t dw[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc = __builtin_fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(dw[e] << 16), acc);
-      acc = __builtin_fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(dw[e] & 0xffff0000u), acc);
+      acc = __builtin_fmaf(T::to_f32(ow[e] & 0xffffu), T::to_f32(dw[e] & 0xffffu), acc);
+      acc = __builtin_fmaf(T::to_f32(ow[e] >> 16), T::to_f32(dw[e] >> 16), acc);
     }
   }
 #pragma unroll
@@ -125,8 +125,8 @@ __device__ __forceinline__ constexpr int roff(int kb, int r) { return 32 * kb + 
 // Transposed-read address (bytes) inside a TileLayout<D> image for the
 // 16-row step kk and 32-column block db: rows 16*kk + tr_row (and +8),
 // columns 32*db + tr_col .. +3 (see lds_read_tr16).
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int kk, int db, int lane) {
+template <typename T, int D>
+__device__ __forceinline__ typename T::vec8 tr_frag(const char* tile, int kk, int db, int lane) {
   using L = TileLayout<D>;
   const int beta = lane >> 4, s16 = lane & 15;
   const int row = 16 * kk + 4 * (beta >> 1) + (s16 >> 2);
@@ -134,14 +134,14 @@ __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int kk, int db, int 
   const int half = 8 * (s16 & 1);
   const char* p0 = tile + L::off(row, chunk) + half;
   const char* p1 = tile + L::off(row + 8, chunk) + half;
-  return cat_frag(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+  return cat_frag<typename T::vec8>(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
                   lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
 }
 
 // A-operand row read (16 bytes) of row `row`, d = 16*ds + 8*g .. +7.
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int ds, int g) {
-  return *reinterpret_cast<const bf16x8*>(tile + TileLayout<D>::off(row, 2 * ds + g));
+template <typename T, int D>
+__device__ __forceinline__ typename T::vec8 row_frag(const char* tile, int row, int ds, int g) {
+  return *reinterpret_cast<const typename T::vec8*>(tile + TileLayout<D>::off(row, 2 * ds + g));
 }
 
 // ---------------------------------------------------------------------------
@@ -159,7 +159,8 @@ struct KVCfg {
 
 // Stores this lane's dS (key row key_row, 64 query columns) into a
 // TileLayout<64> image of dS^T for the dQ product.
-__device__ __forceinline__ void store_ds(char* ds_lds, const bf16x8 (&sf)[2][2], int key_row, int g) {
+template <typename T>
+__device__ __forceinline__ void store_ds(char* ds_lds, const typename T::vec8 (&sf)[2][2], int key_row, int g) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -174,13 +175,13 @@ __device__ __forceinline__ void store_ds(char* ds_lds, const bf16x8 (&sf)[2][2],
 // dP = dO V^T give one key per lane (queries along the accumulator
 // registers); P and dS rounded to bf16 come out as pf / sf, which are the A
 // operands of dV += P^T dO and dK += dS^T Q (dkdv_accum).
-template <int D, int MOD>
+template <typename T, int D, int MOD>
 __device__ __forceinline__ void dkdv_scores(const char* qt_lds, const char* dot_lds, const float* lse_t,
-                                            const float* dl_t, const bf16x8 (&kf)[D / 16],
-                                            const bf16x8 (&vf)[D / 16], const BwdCtx& cx, int q0,
+                                            const float* dl_t, const typename T::vec8 (&kf)[D / 16],
+                                            const typename T::vec8 (&vf)[D / 16], const BwdCtx& cx, int q0,
                                             int my_key, bool masked, int rows_first, int rows_count,
                                             const int* docq_t, bool has_doc, int my_doc,
-                                            bf16x8 (&pf)[2][2], bf16x8 (&sf)[2][2], int lane) {
+                                            typename T::vec8 (&pf)[2][2], typename T::vec8 (&sf)[2][2], int lane) {
   using C = KVCfg<D>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
@@ -196,11 +197,11 @@ __device__ __forceinline__ void dkdv_scores(const char* qt_lds, const char* dot_
     }
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) {
-    bf16x8 qa[2], da[2];
+    typename T::vec8 qa[2], da[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      qa[qb] = row_frag<D>(qt_lds, 32 * qb + c, ds, g);
-      da[qb] = row_frag<D>(dot_lds, 32 * qb + c, ds, g);
+      qa[qb] = row_frag<T, D>(qt_lds, 32 * qb + c, ds, g);
+      da[qb] = row_frag<T, D>(dot_lds, 32 * qb + c, ds, g);
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -256,25 +257,25 @@ __device__ __forceinline__ void dkdv_scores(const char* qt_lds, const char* dot_
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pf[qb][r >> 3][r & 7] = static_cast<__bf16>(s[qb][r]);
-      sf[qb][r >> 3][r & 7] = static_cast<__bf16>(dp[qb][r]);
+      pf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(s[qb][r]);
+      sf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(dp[qb][r]);
     }
 }
 
 // Second half: dV += P^T dO ; dK += dS^T Q (the D/32 output blocks are
 // independent), with transposed reads of the dO and Q tiles.
-template <int D>
-__device__ __forceinline__ void dkdv_accum(const char* qt_lds, const char* dot_lds, const bf16x8 (&pf)[2][2],
-                                           const bf16x8 (&sf)[2][2], f32x16 (&dk)[D / 32],
+template <typename T, int D>
+__device__ __forceinline__ void dkdv_accum(const char* qt_lds, const char* dot_lds, const typename T::vec8 (&pf)[2][2],
+                                           const typename T::vec8 (&sf)[2][2], f32x16 (&dk)[D / 32],
                                            f32x16 (&dv)[D / 32], int lane) {
   using C = KVCfg<D>;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 fo[C::DBLK], fq[C::DBLK];
+    typename T::vec8 fo[C::DBLK], fq[C::DBLK];
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) {
-      fo[db] = tr_frag<D>(dot_lds, kk, db, lane);
-      fq[db] = tr_frag<D>(qt_lds, kk, db, lane);
+      fo[db] = tr_frag<T, D>(dot_lds, kk, db, lane);
+      fq[db] = tr_frag<T, D>(qt_lds, kk, db, lane);
     }
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) {
@@ -284,7 +285,7 @@ __device__ __forceinline__ void dkdv_accum(const char* qt_lds, const char* dot_l
   }
 }
 
-template <int D, int MOD, bool kDq>
+template <typename T, int D, int MOD, bool kDq>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial) {
   using C = KVCfg<D>;
   // Three buffers (one workgroup per CU leaves the LDS room): the copies of
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   const bool k_ok = my_key < a.Sk;
 
   // K and V rows of this lane's key as B operands (d = 16*ds + 8*g .. +7).
-  bf16x8 kf[C::DSTEPS], vf[C::DSTEPS];
+  typename T::vec8 kf[C::DSTEPS], vf[C::DSTEPS];
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) {
     uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
@@ -343,8 +344,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       kr = *reinterpret_cast<const uint4*>(kp + (int64_t)my_key * a.k_ss + 16 * ds + 8 * g);
       vr = *reinterpret_cast<const uint4*>(vp + (int64_t)my_key * a.v_ss + 16 * ds + 8 * g);
     }
-    kf[ds] = __builtin_bit_cast(bf16x8, kr);
-    vf[ds] = __builtin_bit_cast(bf16x8, vr);
+    kf[ds] = __builtin_bit_cast(typename T::vec8, kr);
+    vf[ds] = __builtin_bit_cast(typename T::vec8, vr);
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
 
@@ -455,10 +456,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 af = tr_frag<64>(lds_s, kk, qblk, lane);
+      const typename T::vec8 af = tr_frag<T, 64>(lds_s, kk, qblk, lane);
 #pragma unroll
       for (int j = 0; j < NDB; ++j)
-        acc[j] = mfma32(af, tr_frag<D>(lkk, kk, NDB * (wave >> 1) + j, lane), acc[j]);
+        acc[j] = mfma32(af, tr_frag<T, D>(lkk, kk, NDB * (wave >> 1) + j, lane), acc[j]);
     }
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
@@ -489,9 +490,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     }
     const char* qbuf = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     const char* dbuf = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
-    bf16x8 pf[2][2], sf[2][2];
+    typename T::vec8 pf[2][2], sf[2][2];
     auto scores = [&]() {
-      dkdv_scores<D, MOD>(qbuf, dbuf, BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2),
+      dkdv_scores<T, D, MOD>(qbuf, dbuf, BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2),
                           BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2), kf, vf, cx, qt * C::BM, my_key, masked,
                           rows_first, rows_count, BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2), has_doc, my_doc,
                           pf, sf, lane);
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     if constexpr (!kDq) {
       if (run) {
         scores();
-        dkdv_accum<D>(qbuf, dbuf, pf, sf, dk, dv, lane);
+        dkdv_accum<T, D>(qbuf, dbuf, pf, sf, dk, dv, lane);
       }
     } else {
       if (run) scores();
@@ -509,11 +510,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
 #pragma unroll
           for (int y = 0; y < 2; ++y)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sf[x][y][e] = static_cast<__bf16>(0.0f);
+            for (int e = 0; e < 8; ++e) sf[x][y][e] = static_cast<typename T::elem>(0.0f);
       }
       __syncthreads();  // every wave has finished reading the previous dS^T
-      store_ds(lds_s, sf, 32 * wave + c, g);
-      if (run) dkdv_accum<D>(qbuf, dbuf, pf, sf, dk, dv, lane);
+      store_ds<T>(lds_s, sf, 32 * wave + c, g);
+      if (run) dkdv_accum<T, D>(qbuf, dbuf, pf, sf, dk, dv, lane);
     }
     wait_older(ahead);  // tile t + 1 has landed
     __syncthreads();    // ... for every wave; with kDq also: dS^T is complete
@@ -547,15 +548,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
       } else {
         bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)key * a.dk_ss + kvh * a.dk_sh;
         bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)key * a.dv_ss + kvh * a.dv_sh;
-        dkp[d] = f32_to_bf16(kval);
-        dvp[d] = f32_to_bf16(vval);
+        dkp[d] = f32_to_elem<T>(kval);
+        dvp[d] = f32_to_elem<T>(vval);
       }
     }
   }
 }
 
 // Sum the G per-head partials of each kv head in head order -> bf16.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs a) {
   const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * D;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -574,12 +575,12 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs a) {
   }
   bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)j * a.dk_ss + g * a.dk_sh;
   bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)j * a.dv_ss + g * a.dv_sh;
-  dkp[d] = f32_to_bf16(sk);
-  dvp[d] = f32_to_bf16(sv);
+  dkp[d] = f32_to_elem<T>(sk);
+  dvp[d] = f32_to_elem<T>(sv);
 }
 
 // Non-deterministic dQ: scale the fp32 accumulator and round to bf16.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdArgs a) {
   const int64_t n = (int64_t)a.B * a.Sq * a.Hq * (D / 8);
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -593,10 +594,10 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdArgs a) {
   const float4 x = src[0], y = src[1];
   const float sc = a.scale;
   uint4 o;
-  o.x = f32_to_bf16(x.x * sc) | (uint32_t)f32_to_bf16(x.y * sc) << 16;
-  o.y = f32_to_bf16(x.z * sc) | (uint32_t)f32_to_bf16(x.w * sc) << 16;
-  o.z = f32_to_bf16(y.x * sc) | (uint32_t)f32_to_bf16(y.y * sc) << 16;
-  o.w = f32_to_bf16(y.z * sc) | (uint32_t)f32_to_bf16(y.w * sc) << 16;
+  o.x = f32_to_elem<T>(x.x * sc) | (uint32_t)f32_to_elem<T>(x.y * sc) << 16;
+  o.y = f32_to_elem<T>(x.z * sc) | (uint32_t)f32_to_elem<T>(x.w * sc) << 16;
+  o.z = f32_to_elem<T>(y.x * sc) | (uint32_t)f32_to_elem<T>(y.y * sc) << 16;
+  o.w = f32_to_elem<T>(y.z * sc) | (uint32_t)f32_to_elem<T>(y.w * sc) << 16;
   *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.dq) + b * a.dq_sb + (int64_t)i * a.dq_ss + h * a.dq_sh +
                             part * 8) = o;
 }
@@ -616,9 +617,9 @@ struct QCfg {
 
 // One 64-key tile: S^T = K Q^T and dP^T = V dO^T (one query per lane),
 // dS^T from the saved LSE and Delta, dQ^T += K^T dS^T.
-template <int D, int MOD, bool MASKED>
-__device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, const bf16x8 (&qf)[D / 16],
-                                        const bf16x8 (&df)[D / 16], f32x16 (&dq)[D / 32],
+template <typename T, int D, int MOD, bool MASKED>
+__device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, const typename T::vec8 (&qf)[D / 16],
+                                        const typename T::vec8 (&df)[D / 16], f32x16 (&dq)[D / 32],
                                         const BwdCtx& cx, float lse2, float dl, int my_q, int key_base,
                                         int row_first, int row_count, const int* dock_t, bool has_doc,
                                         int my_doc, int lane) {
@@ -636,11 +637,11 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
     }
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) {
-    bf16x8 ka[2], va[2];
+    typename T::vec8 ka[2], va[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      ka[kb] = row_frag<D>(kt_lds, 32 * kb + c, ds, g);
-      va[kb] = row_frag<D>(vt_lds, 32 * kb + c, ds, g);
+      ka[kb] = row_frag<T, D>(kt_lds, 32 * kb + c, ds, g);
+      va[kb] = row_frag<T, D>(vt_lds, 32 * kb + c, ds, g);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -650,7 +651,7 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
   }
   const uint32_t span = static_cast<uint32_t>(row_count);
   const int jb = key_base + 4 * g - row_first;
-  bf16x8 sf[2][2];
+  typename T::vec8 sf[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -671,20 +672,20 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
         }
         float dsv = p * (dp[kb][r] - dl);
         if (kSoftcap) dsv *= 1.0f - th * th;
-        sf[kb][r >> 3][r & 7] = static_cast<__bf16>(dsv);
+        sf[kb][r >> 3][r & 7] = static_cast<typename T::elem>(dsv);
       }
     }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 ka[C::DBLK];
+    typename T::vec8 ka[C::DBLK];
 #pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) ka[db] = tr_frag<D>(kt_lds, kk, db, lane);
+    for (int db = 0; db < C::DBLK; ++db) ka[db] = tr_frag<T, D>(kt_lds, kk, db, lane);
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) dq[db] = mfma32(ka[db], sf[kk >> 1][kk & 1], dq[db]);
   }
 }
 
-template <int D, int MOD>
+template <typename T, int D, int MOD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(16))) char lk0[C::TB];
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int my_q = qt * C::BM + wave * 32 + c;
   const bool q_ok = my_q < a.Sq;
-  bf16x8 qf[C::DSTEPS], df[C::DSTEPS];
+  typename T::vec8 qf[C::DSTEPS], df[C::DSTEPS];
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) {
     uint4 r1 = make_uint4(0, 0, 0, 0), r2 = make_uint4(0, 0, 0, 0);
@@ -722,8 +723,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       r1 = *reinterpret_cast<const uint4*>(qp + (int64_t)my_q * a.q_ss + 16 * ds + 8 * g);
       r2 = *reinterpret_cast<const uint4*>(dop + (int64_t)my_q * a.do_ss + 16 * ds + 8 * g);
     }
-    qf[ds] = __builtin_bit_cast(bf16x8, r1);
-    df[ds] = __builtin_bit_cast(bf16x8, r2);
+    qf[ds] = __builtin_bit_cast(typename T::vec8, r1);
+    df[ds] = __builtin_bit_cast(typename T::vec8, r2);
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
   float lse2 = kPosInf, dl = 0.0f;
@@ -796,7 +797,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int kt = kt_of(t);
     const bool has_next = t + 1 < ntiles;
     if (has_next) load_tile(kt_of(t + 1), NEXT{});
-    dq_tile<D, MOD, decltype(masked)::value>(BUF ? lk1 : lk0, BUF ? lv1 : lv0, qf, df, dq, cx, lse2, dl,
+    dq_tile<T, D, MOD, decltype(masked)::value>(BUF ? lk1 : lk0, BUF ? lv1 : lv0, qf, df, dq, cx, lse2, dl,
                                              my_q, kt * C::BN, row_first, row_count, BUF ? lz1 : lz0,
                                              has_doc, my_doc, lane);
     wait_dma();
@@ -826,15 +827,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * db + 8 * rr + 4 * g;
         uint2 packed;
-        packed.x = f32_to_bf16(dq[db][4 * rr] * scale) | (uint32_t)f32_to_bf16(dq[db][4 * rr + 1] * scale) << 16;
-        packed.y = f32_to_bf16(dq[db][4 * rr + 2] * scale) | (uint32_t)f32_to_bf16(dq[db][4 * rr + 3] * scale) << 16;
+        packed.x = f32_to_elem<T>(dq[db][4 * rr] * scale) | (uint32_t)f32_to_elem<T>(dq[db][4 * rr + 1] * scale) << 16;
+        packed.y = f32_to_elem<T>(dq[db][4 * rr + 2] * scale) | (uint32_t)f32_to_elem<T>(dq[db][4 * rr + 3] * scale) << 16;
         *reinterpret_cast<uint2*>(out + d0) = packed;
       }
     }
   }
 }
 
-template <int D, int MOD>
+template <typename T, int D, int MOD>
 hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int partial = G > 1 ? 1 : 0;
@@ -842,15 +843,15 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   const bool atomic_dq = a.dq_acc != nullptr;
   if ((stages & 2) && nkt > 0) {
     if (atomic_dq)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, MOD, true>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, true>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((stages & 4) && partial && a.Sk > 0) {
     const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * D;
-    hipLaunchKernelGGL(bwd_group_sum_kernel<D>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_group_sum_kernel<T, D>), dim3((n + 255) / 256), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -858,19 +859,19 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   if (!(stages & 8) || nqt == 0) return hipSuccess;
   if (atomic_dq) {
     const int64_t n = (int64_t)a.B * a.Sq * a.Hq * (D / 8);
-    hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3((n + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), dim3((n + 255) / 256), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, MOD>), dim3(nqt * a.Hq * a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MOD>), dim3(nqt * a.Hq * a.B), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
   constexpr int LPR = D / 8;
   if ((stages & 1) && rows > 0) {
-    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((rows * LPR + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((rows * LPR + 255) / 256), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -878,14 +879,14 @@ hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
   const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0) |
                   (a.tiles.kv_num_full != nullptr ? 4 : 0);
   switch (mod) {
-    case 0: return launch_mod<D, 0>(a, stages, s);
-    case 1: return launch_mod<D, 1>(a, stages, s);
-    case 2: return launch_mod<D, 2>(a, stages, s);
-    case 3: return launch_mod<D, 3>(a, stages, s);
-    case 4: return launch_mod<D, 4>(a, stages, s);
-    case 5: return launch_mod<D, 5>(a, stages, s);
-    case 6: return launch_mod<D, 6>(a, stages, s);
-    default: return launch_mod<D, 7>(a, stages, s);
+    case 0: return launch_mod<T, D, 0>(a, stages, s);
+    case 1: return launch_mod<T, D, 1>(a, stages, s);
+    case 2: return launch_mod<T, D, 2>(a, stages, s);
+    case 3: return launch_mod<T, D, 3>(a, stages, s);
+    case 4: return launch_mod<T, D, 4>(a, stages, s);
+    case 5: return launch_mod<T, D, 5>(a, stages, s);
+    case 6: return launch_mod<T, D, 6>(a, stages, s);
+    default: return launch_mod<T, D, 7>(a, stages, s);
   }
 }
 
@@ -901,8 +902,9 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int stage_mask, hipStream_t s) {
   if (a.B == 0 || a.Hq == 0) return hipSuccess;
-  if (a.D == 64) return launch_d<64>(a, stage_mask, s);
-  return launch_d<128>(a, stage_mask, s);
+  if (a.f16) return a.D == 64 ? launch_d<F16T, 64>(a, stage_mask, s) : launch_d<F16T, 128>(a, stage_mask, s);
+  if (a.D == 64) return launch_d<Bf16T, 64>(a, stage_mask, s);
+  return launch_d<Bf16T, 128>(a, stage_mask, s);
 }
 
 }  // namespace attn

@@ -9,6 +9,7 @@ namespace attn {
 typedef uint16_t bf16_t;  // storage type of bfloat16 tensors
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -40,6 +41,29 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// The same shape with fp16 operands (identical operand and result layouts).
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// 16-bit input element types of the matrix-core kernels.  Both are stored as
+// 16-bit patterns (bf16_t); kernels take one of these as a template
+// parameter and use vec8 for MFMA operands and elem for conversions (both
+// conversions from fp32 round to nearest even).
+struct Bf16T {
+  using vec8 = bf16x8;
+  using elem = __bf16;
+  __device__ static float to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+};
+struct F16T {
+  using vec8 = f16x8;
+  using elem = _Float16;
+  __device__ static float to_f32(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
+};
+template <typename T>
+__device__ __forceinline__ uint16_t f32_to_elem(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<typename T::elem>(f));
+}
 
 // LDS transposed read (ds_read_b64_tr_b16).  Within each 16-lane block,
 // lane i receives element i%4 of the 8-byte chunks addressed by lanes
@@ -54,9 +78,10 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const bf16_t* p) {
 // Concatenate two transposed reads into one MFMA operand.  Done as a whole-
 // vector shuffle and bit cast: assembling the bf16 vector element by element
 // from 16-bit integer lanes was compiled into code that kept only element 0.
-__device__ __forceinline__ bf16x8 cat_frag(i16x4 lo, i16x4 hi) {
+template <typename V = bf16x8>
+__device__ __forceinline__ V cat_frag(i16x4 lo, i16x4 hi) {
   const i16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
+  return __builtin_bit_cast(V, c);
 }
 
 __device__ __forceinline__ float wave_xor32(float x) {

@@ -1,4 +1,4 @@
-// Split-K decode over a KV cache, bf16 (gfx950).
+// Split-K decode over a KV cache, bf16 or fp16 (gfx950).
 //
 // flash_attn_with_kvcache ("FlashAttention: Fast and Memory-Efficient Exact
 // Attention", "Examples") attends the new queries of each sequence (one, or a
@@ -178,7 +178,7 @@ struct Cursor {
   int left;                       // K/V steps left in this workgroup's range
 };
 
-template <int D, bool kSoftcap, bool kMulti>
+template <typename T, int D, bool kSoftcap, bool kMulti>
 __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeArgs a) {
   using C = DecCfg<D>;
   using L = typename C::L;
@@ -393,14 +393,14 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   const int tr_chunk = 2 * (beta & 1) + ((s16 & 3) >> 1);
   const int tr_half = 8 * (s16 & 1);
 
-  bf16x8 qf[C::DSTEPS];
+  typename T::vec8 qf[C::DSTEPS];
   float m_run = kNegInf, l_run = 0.0f;  // m_run in exp2 units
   // kMulti (causal, several queries): keys this lane's row may see, and the
   // smallest such count in the wave (steps below it need no mask).
   int lim_row = 0, lim_wave = 0;
   f32x16 oacc[C::DBLK];
 #pragma unroll
-  for (int ds = 0; ds < C::DSTEPS; ++ds) qf[ds] = bf16x8{};
+  for (int ds = 0; ds < C::DSTEPS; ++ds) qf[ds] = __builtin_bit_cast(typename T::vec8, make_uint4(0, 0, 0, 0));
 #pragma unroll
   for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
@@ -420,10 +420,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const char* kt = ring + ((i0 + t) % C::NS) * C::SB;
-      bf16x8 ka[C::DSTEPS];
+      typename T::vec8 ka[C::DSTEPS];
 #pragma unroll
       for (int ds = 0; ds < C::DSTEPS; ++ds)
-        ka[ds] = *reinterpret_cast<const bf16x8*>(kt + L::off(c, 2 * ds + g));
+        ka[ds] = *reinterpret_cast<const typename T::vec8*>(kt + L::off(c, 2 * ds + g));
 #pragma unroll
       for (int ds = 0; ds < C::DSTEPS; ++ds) sacc[t] = mfma32(ka[ds], qf[ds], sacc[t]);
     }
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
     }
-    bf16x8 pf[NI][2];
+    typename T::vec8 pf[NI][2];
     float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     // (A row with no visible key yet keeps m_run = -inf; all its scores are
     // -inf then, and a zero reference keeps exp2 at 0 instead of NaN.)
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         ls[r & 3] += p[r];
-        pf[t][r >> 3][r & 7] = static_cast<__bf16>(p[r]);
+        pf[t][r >> 3][r & 7] = static_cast<typename T::elem>(p[r]);
       }
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -505,12 +505,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       const char* vt = ring + ((i0 + t) % C::NS) * C::SB + C::TB;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 va[C::DBLK];
+        typename T::vec8 va[C::DBLK];
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db) {
           const char* p0 = vt + L::off(16 * ks + tr_row, 4 * db + tr_chunk) + tr_half;
           const char* p1 = vt + L::off(16 * ks + 8 + tr_row, 4 * db + tr_chunk) + tr_half;
-          va[db] = cat_frag(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+          va[db] = cat_frag<typename T::vec8>(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
                             lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
         }
 #pragma unroll
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
           raw.y ^= qsign;
           raw.z ^= qsign;
           raw.w ^= qsign;
-          qf[ds] = __builtin_bit_cast(bf16x8, raw);
+          qf[ds] = __builtin_bit_cast(typename T::vec8, raw);
         }
       }
       if (lane == 0) publish(&consumed[wave], i + gsz);
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 // Merge the partial results of one job: one thread per (head row, 4 columns).
 // The job's partials are in slots w + j for w from its first to its last
 // workgroup, as recorded by the split kernel.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int TPH = D / 4;      // threads per head
   constexpr int HPB = 256 / TPH;  // heads per workgroup
@@ -735,10 +735,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
   const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
   bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)t * a.o_ss + (int64_t)h * a.o_sh + 4 * d4;
-  const uint32_t lo2 = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.x * inv)) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.y * inv)) << 16);
-  const uint32_t hi2 = (uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.z * inv)) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, f32_to_bf16(acc.w * inv)) << 16);
+  const uint32_t lo2 = (uint32_t)(f32_to_elem<T>(acc.x * inv)) |
+                       ((uint32_t)(f32_to_elem<T>(acc.y * inv)) << 16);
+  const uint32_t hi2 = (uint32_t)(f32_to_elem<T>(acc.z * inv)) |
+                       ((uint32_t)(f32_to_elem<T>(acc.w * inv)) << 16);
   *reinterpret_cast<uint2*>(op) = make_uint2(lo2, hi2);
   if (d4 == 0) a.lse[((int64_t)b * a.Hq + h) * a.Sq + t] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
 }
@@ -777,7 +777,7 @@ __global__ __launch_bounds__(256) void kvcache_append_kernel(DecodeArgs a) {
   *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
 }
 
-template <int D>
+template <typename T, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   if (a.len_add > 0) {
     const int64_t total = (int64_t)a.B * a.len_add * a.Hkv * (D / 8);
@@ -788,17 +788,17 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   const dim3 block(DecCfg<D>::NT);
   const bool multi = a.causal && a.Sq > 1;
   if (a.softcap > 0.0f) {
-    if (multi) hipLaunchKernelGGL((decode_split_kernel<D, true, true>), dim3(a.parts), block, 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<D, true, false>), dim3(a.parts), block, 0, s, a);
+    if (multi) hipLaunchKernelGGL((decode_split_kernel<T, D, true, true>), dim3(a.parts), block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), dim3(a.parts), block, 0, s, a);
   } else {
-    if (multi) hipLaunchKernelGGL((decode_split_kernel<D, false, true>), dim3(a.parts), block, 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<D, false, false>), dim3(a.parts), block, 0, s, a);
+    if (multi) hipLaunchKernelGGL((decode_split_kernel<T, D, false, true>), dim3(a.parts), block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), dim3(a.parts), block, 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int HPB = 256 / (D / 4);
   const int jobs = a.B * a.Hkv * a.nhg;
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(jobs, (DecCfg<D>::ROWS + HPB - 1) / HPB), dim3(256),
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(jobs, (DecCfg<D>::ROWS + HPB - 1) / HPB), dim3(256),
                      0, s, a);
   return hipGetLastError();
 }
@@ -836,8 +836,9 @@ DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int part
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  if (a.D == 64) return launch_d<64>(a, s);
-  return launch_d<128>(a, s);
+  if (a.f16) return a.D == 64 ? launch_d<F16T, 64>(a, s) : launch_d<F16T, 128>(a, s);
+  if (a.D == 64) return launch_d<Bf16T, 64>(a, s);
+  return launch_d<Bf16T, 128>(a, s);
 }
 
 }  // namespace attn

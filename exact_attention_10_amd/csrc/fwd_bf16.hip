@@ -1,4 +1,4 @@
-// Forward attention, bf16 inputs, MFMA (gfx950).
+// Forward attention, bf16 or fp16 inputs, MFMA (gfx950).
 //
 // Tiled exact attention with an online softmax ("Accelerating AI: A Deep
 // Dive into Flash Attention", sections "Tiling the Computation",
@@ -55,8 +55,9 @@ struct Tile {
   bool full;
 };
 
-__device__ __forceinline__ bf16x8 zero_frag() {
-  return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+template <typename V>
+__device__ __forceinline__ V zero_frag() {
+  return __builtin_bit_cast(V, make_uint4(0, 0, 0, 0));
 }
 
 struct TileCtx {
@@ -77,9 +78,9 @@ __device__ __forceinline__ constexpr int koff(int kb, int r) { return 32 * kb + 
 
 // One 64-key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
 // MASKED evaluates the mask predicate per element (partial tiles only).
-template <int D, int MOD, bool MASKED>
+template <typename T, int D, int MOD, bool MASKED>
 __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_base,
-                                         const int* doc_t, const bf16x8 (&qf)[D / 16],
+                                         const int* doc_t, const typename T::vec8 (&qf)[D / 16],
                                          f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
                                          const TileCtx& cx, int key_base, int lane) {
   using C = FwdCfg<D>;
@@ -98,12 +99,12 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
     for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ds += 2) {
-    bf16x8 ka[2][2];
+    typename T::vec8 ka[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        ka[kb][u] = *reinterpret_cast<const bf16x8*>(kb_base + C::L::off(32 * kb + c, 2 * (ds + u) + g));
+        ka[kb][u] = *reinterpret_cast<const typename T::vec8*>(kb_base + C::L::off(32 * kb + c, 2 * (ds + u) + g));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -174,8 +175,8 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
   }
   const float msub = (m_run == kNegInf) ? 0.0f : m_run;
 
-  // P = exp2(x - m), packed to bf16 as the B operand of O^T += V^T P^T.
-  bf16x8 pf[2][2];
+  // P = exp2(x - m), rounded to the input type as the B operand of O^T += V^T P^T.
+  typename T::vec8 pf[2][2];
   float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -184,7 +185,7 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
       const float p = kScaled ? fast_exp2(sacc[kb][r] - msub)
                               : fast_exp2(__builtin_fmaf(sacc[kb][r], cx.scale_log2, -msub));
       ls[r & 3] += p;
-      pf[kb][r >> 3][r & 7] = static_cast<__bf16>(p);
+      pf[kb][r >> 3][r & 7] = static_cast<typename T::elem>(p);
     }
   l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
@@ -197,12 +198,12 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
   const int tr_half = 8 * (s16 & 1);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 va[C::DBLK];
+    typename T::vec8 va[C::DBLK];
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) {
       const char* p0 = vb_base + C::L::off(16 * kk + tr_row, 4 * db + tr_chunk) + tr_half;
       const char* p1 = vb_base + C::L::off(16 * kk + 8 + tr_row, 4 * db + tr_chunk) + tr_half;
-      va[db] = cat_frag(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+      va[db] = cat_frag<typename T::vec8>(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
                         lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
     }
 #pragma unroll
@@ -213,7 +214,7 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
 // NW waves of 32 query rows: 4 (128 rows, two workgroups per CU) or 8 (256
 // rows, one workgroup per CU; each K/V tile copied to LDS feeds twice the
 // query rows, halving the L2-to-LDS traffic per flop).
-template <int D, int MOD, int NW>  // MOD bit 0: ALiBi, bit 1: softcap
+template <typename T, int D, int MOD, int NW>  // MOD bit 0: ALiBi, bit 1: softcap
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D, NW>;
   constexpr bool kAlibi = MOD & 1;
@@ -262,15 +263,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // positive and row maxima can be taken on the raw dot products.
   const float scale_abs = fabsf(a.scale);
   const uint32_t sign_flip = a.scale < 0.0f ? 0x80008000u : 0u;
-  bf16x8 qf[C::DSTEPS];
+  typename T::vec8 qf[C::DSTEPS];
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) {
     if (q_ok) {
       uint4 raw = *reinterpret_cast<const uint4*>(qp + (int64_t)my_q * a.q_ss + 16 * ds + 8 * g);
       raw.x ^= sign_flip; raw.y ^= sign_flip; raw.z ^= sign_flip; raw.w ^= sign_flip;
-      qf[ds] = __builtin_bit_cast(bf16x8, raw);
+      qf[ds] = __builtin_bit_cast(typename T::vec8, raw);
     } else {
-      qf[ds] = zero_frag();
+      qf[ds] = zero_frag<typename T::vec8>();
     }
   }
 
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
       else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
     }
-    fwd_tile<D, MOD, decltype(masked)::value>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
+    fwd_tile<T, D, MOD, decltype(masked)::value>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
                                               BUF ? lds_doc1 : lds_doc0, qf, oacc, m_run, l_run,
                                               ctx, cur.kt * C::BN, lane);
     if (has_next) store_doc(NEXT{});
@@ -419,8 +420,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * db + 8 * rr + 4 * g;
         uint2 packed;
-        packed.x = f32_to_bf16(oacc[db][4 * rr + 0] * inv) | (uint32_t)f32_to_bf16(oacc[db][4 * rr + 1] * inv) << 16;
-        packed.y = f32_to_bf16(oacc[db][4 * rr + 2] * inv) | (uint32_t)f32_to_bf16(oacc[db][4 * rr + 3] * inv) << 16;
+        packed.x = f32_to_elem<T>(oacc[db][4 * rr + 0] * inv) | (uint32_t)f32_to_elem<T>(oacc[db][4 * rr + 1] * inv) << 16;
+        packed.y = f32_to_elem<T>(oacc[db][4 * rr + 2] * inv) | (uint32_t)f32_to_elem<T>(oacc[db][4 * rr + 3] * inv) << 16;
         *reinterpret_cast<uint2*>(op + d0) = packed;
       }
     }
@@ -430,17 +431,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int NW>
+template <typename T, int D, int NW>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int bm = 32 * NW;
   const int nqt = (a.Sq + bm - 1) / bm;
   const dim3 grid(nqt * a.Hq * a.B), block(64 * NW);
   const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0);
   switch (mod) {
-    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, NW>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, NW>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, NW>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, 3, NW>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 0, NW>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 1, NW>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 2, NW>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 3, NW>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -461,8 +462,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   if (a.Sq == 0 || a.B == 0 || a.Hq == 0) return hipSuccess;
   const bool sparse = a.tiles.kv_num_full != nullptr;
   const bool wide = fwd_bf16_rows_per_block(a.B, a.Sq, a.Hq, a.mask.causal, sparse) == 256;
-  if (a.D == 64) return wide ? launch_d<64, 8>(a, s) : launch_d<64, 4>(a, s);
-  return wide ? launch_d<128, 8>(a, s) : launch_d<128, 4>(a, s);
+  if (a.f16) {
+    if (a.D == 64) return wide ? launch_d<F16T, 64, 8>(a, s) : launch_d<F16T, 64, 4>(a, s);
+    return wide ? launch_d<F16T, 128, 8>(a, s) : launch_d<F16T, 128, 4>(a, s);
+  }
+  if (a.D == 64) return wide ? launch_d<Bf16T, 64, 8>(a, s) : launch_d<Bf16T, 64, 4>(a, s);
+  return wide ? launch_d<Bf16T, 128, 8>(a, s) : launch_d<Bf16T, 128, 4>(a, s);
 }
 
 }  // namespace attn

@@ -27,6 +27,7 @@ struct TileLists {
 
 struct FwdArgs {
   const void* q; const void* k; const void* v; void* o;
+  bool f16;                  // 16-bit inputs are fp16 (else bf16); the fp32 kernel ignores it
   float* lse;
   uint8_t* trace;
   int64_t q_sb, q_ss, q_sh;
@@ -68,6 +69,7 @@ struct BwdTiles {
 
 struct BwdArgs {
   const void* q; const void* k; const void* v; const void* o; const void* dout;
+  bool f16;                  // inputs and gradients are fp16 (else bf16)
   const float* lse;
   void* dq; void* dk; void* dv;
   int64_t q_sb, q_ss, q_sh;
@@ -98,6 +100,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int stage_mask, hipStream_t s);
 
 struct DecodeArgs {
   const void* q; const void* k; const void* v; void* o;
+  bool f16;                  // q, caches, new rows and o are fp16 (else bf16)
   float* lse;
   const int32_t* seqlens;
   int64_t q_sb, q_ss, q_sh;

@@ -6,7 +6,7 @@ attention arithmetic.  Every workload draws from
 data first (document lengths, cache lengths), then q, k, v, then the output
 gradient dO, each as float32 standard normals.  bf16 workloads round those
 float32 draws to bfloat16 (round to nearest, ties to even) and keep the raw
-16-bit patterns; both the GPU path and the fp64 CPU check consume exactly
+16-bit patterns (fp16 workloads likewise round to IEEE half); both the GPU path and the fp64 CPU check consume exactly
 those patterns.
 
 The shapes are those of the pages' workloads: Llama-3.1-8B attention (32
@@ -42,6 +42,16 @@ def bf16_bits_to_f64(bits):
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
+def f32_to_f16_bits(x):
+    """Round float32 values to IEEE half, nearest-even (numpy's cast);
+    returns uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f64(bits):
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
 # ---------------------------------------------------------------------------
 # workloads
 
@@ -54,7 +64,11 @@ class Workload(dict):
 
 def _normals(rng, shape, dtype):
     x = rng.standard_normal(shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f16":
+        return f32_to_f16_bits(x)
+    return x
 
 
 def doc_lengths(rng, S, lo=256, hi=2048):
@@ -179,4 +193,6 @@ def as_f64(x, dtype):
     """The values a consumer of stored inputs sees, widened to fp64."""
     if dtype == "bf16":
         return bf16_bits_to_f64(x)
+    if dtype == "f16":
+        return f16_bits_to_f64(x)
     return np.asarray(x, dtype=np.float64)

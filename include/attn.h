@@ -52,9 +52,14 @@
  *    accepted, so [B, H, S, D] views ([GYM] transposes q/k/v to that layout
  *    for flex_attention) and packed-QKV slices ([FA] qkv of shape
  *    (batch, seqlen, 3, nheads, headdim)) are read in place.
- *  - Supported head dims: 64 and 128.  Supported dtypes: ATTN_BF16 for all
- *    entry points; ATTN_FP32 for attn_fwd (computed in fp32 on the vector
- *    ALU).  Every tensor of one call has the same dtype.
+ *    Gradients are written the same way, so dq/dk/dv may be slices of one
+ *    packed dqkv tensor.
+ *  - Supported head dims: 64 and 128.  Supported dtypes: ATTN_BF16 and
+ *    ATTN_FP16 for all entry points ([TA] "FP16 vs. BF16 Representation": both
+ *    16-bit types;
+ *    fp32 accumulation, probabilities and dS rounded to the input type as
+ *    matrix-core operands); ATTN_FP32 for attn_fwd (computed in fp32 on the
+ *    vector ALU).  Every tensor of one call has the same dtype.
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H
@@ -74,7 +79,7 @@ typedef enum {
   ATTN_ERR_HIP = 4            /* the HIP runtime reported an error */
 } attn_status;
 
-typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype;
+typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1, ATTN_FP16 = 2 } attn_dtype;
 
 typedef struct {
   void* data;          /* device pointer to element [0,0,0,0] */

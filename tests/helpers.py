@@ -12,9 +12,11 @@ GRAD_ATOL = 5e-2
 
 
 def to_device(arr, dtype, torch, device="cuda"):
-    """Stored inputs (bf16 bit patterns or fp32) -> torch tensor on `device`."""
+    """Stored inputs (bf16 / fp16 bit patterns or fp32) -> torch tensor on `device`."""
     if dtype == "bf16":
         t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.float16)
     else:
         t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
     return t.to(device)

@@ -218,3 +218,46 @@ def test_bwd_nondeterministic_llama8b_full(b):
     dq1, dk1, dv1 = run_bwd(b, w, **kw)
     assert torch.equal(dk, dk1) and torch.equal(dv, dv1)
     assert float((dq.float() - dq1.float()).abs().max()) <= 1e-2
+
+
+# ---------------------------------------------------------------------------
+# Packed inputs and gradients ([FA] flash_attn_qkvpacked_func /
+# flash_attn_kvpacked_func): the kernels read and write through strides, so
+# packed tensors are used in place and the results are bitwise those of the
+# separate tensors.
+
+@pytest.mark.parametrize("D,causal", [(64, True), (128, False)])
+def test_qkvpacked_fwd_bwd(b, D, causal):
+    B, S, H = 2, 333, 4
+    w = inputs.random_case(900 + D, B, S, S, H, H, D, dtype="bf16", grad=True)
+    q, k, v, do = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v", "do"))
+    qkv = torch.stack([q, k, v], dim=2).contiguous()  # [B, S, 3, H, D]
+    o_p, lse_p = b.attn_fwd_qkvpacked(qkv, softmax_scale=0.1, causal=causal)
+    dqkv = b.attn_bwd_qkvpacked(qkv, o_p, do, lse_p, softmax_scale=0.1, causal=causal)
+    o, lse = b.attn_fwd(q, k, v, softmax_scale=0.1, causal=causal)
+    dq, dk, dv = b.attn_bwd(q, k, v, o, do, lse, softmax_scale=0.1, causal=causal)
+    torch.cuda.synchronize()
+    assert dqkv.shape == qkv.shape
+    assert torch.equal(o_p, o) and torch.equal(lse_p, lse)
+    assert torch.equal(dqkv[:, :, 0], dq) and torch.equal(dqkv[:, :, 1], dk) and torch.equal(dqkv[:, :, 2], dv)
+    rq, rk, rv = oracle.attention_bwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), f64(w, "do"), scale=0.1,
+                                      causal=causal)
+    check_o(to_f64(dqkv[:, :, 0]), rq, GRAD_ATOL, "dQ")
+    check_o(to_f64(dqkv[:, :, 1]), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dqkv[:, :, 2]), rv, GRAD_ATOL, "dV")
+
+
+def test_kvpacked_gqa(b):
+    B, S, Hq, Hkv, D = 1, 300, 8, 2, 128
+    w = inputs.random_case(950, B, S, S, Hq, Hkv, D, dtype="bf16", grad=True)
+    q, k, v, do = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v", "do"))
+    kv = torch.stack([k, v], dim=2).contiguous()  # [B, S, 2, Hkv, D]
+    o, lse = b.attn_fwd_kvpacked(q, kv, softmax_scale=0.09, causal=True)
+    dq, dkv = b.attn_bwd_kvpacked(q, kv, o, do, lse, softmax_scale=0.09, causal=True)
+    dq2, dk2, dv2 = run_bwd(b, w, softmax_scale=0.09, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dkv[:, :, 0], dk2) and torch.equal(dkv[:, :, 1], dv2)
+    rq, rk, rv = oracle.attention_bwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), f64(w, "do"), scale=0.09,
+                                      causal=True)
+    check_o(to_f64(dkv[:, :, 0]), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dkv[:, :, 1]), rv, GRAD_ATOL, "dV")

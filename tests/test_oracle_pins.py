@@ -630,6 +630,15 @@ def test_seeded_workload_side_data():
     assert int(lens.sum()) == 138534
 
 
+def test_f16_rounding_helpers():
+    """IEEE half: 11 significant bits, ties to even, max 65504."""
+    x = np.array([1.0, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -2.5, 65504.0, 2.0 ** -24], dtype=np.float32)
+    bits = inputs.f32_to_f16_bits(x)
+    back = inputs.f16_bits_to_f64(bits)
+    np.testing.assert_array_equal(back, [1.0, 1.0, 1.0 + 2.0 ** -9, -2.5, 65504.0, 2.0 ** -24])
+    assert bits[0] == 0x3C00 and bits[3] == 0xC100
+
+
 def test_bf16_rounding_helpers():
     x = np.array([1.0, 1.00390625, 1.005859375, -2.5, 3.0e38, 1e-40], dtype=np.float32)
     bits = inputs.f32_to_bf16_bits(x)
