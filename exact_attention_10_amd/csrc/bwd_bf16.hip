@@ -337,15 +337,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
 
   // K and V rows of this lane's key as B operands (d = 16*ds + 8*g .. +7).
   typename T::vec8 kf[C::DSTEPS], vf[C::DSTEPS];
+  // All loads are issued before any is used (a key past Sk reads key Sk - 1
+  // and is zeroed after): guarded one by one they became a chain of waited
+  // round trips.
+  {
+    const int key_row = k_ok ? my_key : a.Sk - 1;
+    uint4 kr[C::DSTEPS], vr[C::DSTEPS];
 #pragma unroll
-  for (int ds = 0; ds < C::DSTEPS; ++ds) {
-    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-    if (k_ok) {
-      kr = *reinterpret_cast<const uint4*>(kp + (int64_t)my_key * a.k_ss + 16 * ds + 8 * g);
-      vr = *reinterpret_cast<const uint4*>(vp + (int64_t)my_key * a.v_ss + 16 * ds + 8 * g);
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      kr[ds] = *reinterpret_cast<const uint4*>(kp + (int64_t)key_row * a.k_ss + 16 * ds + 8 * g);
+      vr[ds] = *reinterpret_cast<const uint4*>(vp + (int64_t)key_row * a.v_ss + 16 * ds + 8 * g);
     }
-    kf[ds] = __builtin_bit_cast(typename T::vec8, kr);
-    vf[ds] = __builtin_bit_cast(typename T::vec8, vr);
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      kf[ds] = __builtin_bit_cast(typename T::vec8, k_ok ? kr[ds] : z);
+      vf[ds] = __builtin_bit_cast(typename T::vec8, k_ok ? vr[ds] : z);
+    }
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
 
@@ -389,12 +397,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   // is given, else lse2 again), so one counter value means "all but the
   // newest tile have landed".
   constexpr int kOpsPerTile = 2 * (64 / C::L::RG / 4) + 1;
+  const TileCopy<D> qcopy(qp, a.q_ss, a.Sq, wave, lane);
+  const TileCopy<D> docopy(dop, a.do_ss, a.Sq, wave, lane);
   auto load_tile = [&](int qt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
-    tile_dma<D>(reinterpret_cast<bf16_t*>(qd), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
-    tile_dma<D>(reinterpret_cast<bf16_t*>(dd), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
+    qcopy(reinterpret_cast<bf16_t*>(qd), qt * C::BM);
+    docopy(reinterpret_cast<bf16_t*>(dd), qt * C::BM);
     // rows past Sq repeat the last row; they are masked on partial tiles
     const int i = min(qt * C::BM + lane, a.Sq - 1);
     const void* src;
@@ -716,23 +726,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int my_q = qt * C::BM + wave * 32 + c;
   const bool q_ok = my_q < a.Sq;
   typename T::vec8 qf[C::DSTEPS], df[C::DSTEPS];
+  // (All loads issued before any use; rows past Sq read row Sq - 1 and are
+  // zeroed after.)
+  const int q_row = q_ok ? my_q : a.Sq - 1;
+  {
+    uint4 r1[C::DSTEPS], r2[C::DSTEPS];
 #pragma unroll
-  for (int ds = 0; ds < C::DSTEPS; ++ds) {
-    uint4 r1 = make_uint4(0, 0, 0, 0), r2 = make_uint4(0, 0, 0, 0);
-    if (q_ok) {
-      r1 = *reinterpret_cast<const uint4*>(qp + (int64_t)my_q * a.q_ss + 16 * ds + 8 * g);
-      r2 = *reinterpret_cast<const uint4*>(dop + (int64_t)my_q * a.do_ss + 16 * ds + 8 * g);
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      r1[ds] = *reinterpret_cast<const uint4*>(qp + (int64_t)q_row * a.q_ss + 16 * ds + 8 * g);
+      r2[ds] = *reinterpret_cast<const uint4*>(dop + (int64_t)q_row * a.do_ss + 16 * ds + 8 * g);
     }
-    qf[ds] = __builtin_bit_cast(typename T::vec8, r1);
-    df[ds] = __builtin_bit_cast(typename T::vec8, r2);
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      qf[ds] = __builtin_bit_cast(typename T::vec8, q_ok ? r1[ds] : z);
+      df[ds] = __builtin_bit_cast(typename T::vec8, q_ok ? r2[ds] : z);
+    }
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
-  float lse2 = kPosInf, dl = 0.0f;
-  if (q_ok) {
-    const float l = a.lse[((int64_t)b * a.Hq + h) * a.Sq + my_q];
-    lse2 = l == kNegInf ? kPosInf : l * kLog2e;
-    dl = a.delta[((int64_t)b * a.Hq + h) * a.Sq + my_q];
-  }
+  const float l_row = a.lse[((int64_t)b * a.Hq + h) * a.Sq + q_row];
+  const float d_row = a.delta[((int64_t)b * a.Hq + h) * a.Sq + q_row];
+  const float lse2 = !q_ok || l_row == kNegInf ? kPosInf : l_row * kLog2e;
+  const float dl = q_ok ? d_row : 0.0f;
 
   // Key tiles in processing order, FULL ones first.  Dense: the interval of
   // the causal / window band.  Block-sparse: the mask's FULL then PARTIAL
@@ -768,10 +783,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // K and V of tile kt into buffer BUF, and (document masks) the tile's 64
   // key document ids, copied by wave 0; every wait below is a full one.
+  const TileCopy<D> kcopy(kp, a.k_ss, a.Sk, wave, lane);
+  const TileCopy<D> vcopy(vp, a.v_ss, a.Sk, wave, lane);
   auto load_tile = [&](int kt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
-    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lk1 : lk0), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
-    tile_dma<D>(reinterpret_cast<bf16_t*>(BUF ? lv1 : lv0), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
+    kcopy(reinterpret_cast<bf16_t*>(BUF ? lk1 : lk0), kt * C::BN);
+    vcopy(reinterpret_cast<bf16_t*>(BUF ? lv1 : lv0), kt * C::BN);
     if (has_doc && wave == 0) {
       const int j = min(kt * C::BN + lane, a.Sk - 1);  // keys past Sk are masked
       __builtin_amdgcn_global_load_lds(dock + j, (__attribute__((address_space(3))) void*)(BUF ? lz1 : lz0),

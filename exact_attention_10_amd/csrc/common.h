@@ -167,6 +167,37 @@ __device__ __forceinline__ void tile_dma(bf16_t* tile, const bf16_t* src, int64_
   }
 }
 
+// The same copy with the per-lane part of the address computed once: a tile
+// at row0 then costs one scalar base and one 64-bit add per copy (the
+// clamping form above is kept for a tile that runs past nrows).
+template <int D, int NW = 4>
+struct TileCopy {
+  using L = TileLayout<D>;
+  static constexpr int NU = 64 / L::RG / NW;  // copies per lane per tile
+  static_assert((64 / L::RG) % NW == 0, "groups must divide among the waves");
+  const bf16_t* src;
+  int64_t ld;
+  int64_t lane_off;  // bytes from a tile's first row to this lane's 16 bytes (copy 0)
+  int nrows, wave, lane;
+  __device__ TileCopy(const bf16_t* src_, int64_t ld_, int nrows_, int wave_, int lane_)
+      : src(src_), ld(ld_), nrows(nrows_), wave(wave_), lane(lane_) {
+    lane_off = ((int64_t)(wave_ * L::RG + lane_ % L::RG) * ld_ + (lane_ / L::RG) * 8) * 2;
+  }
+  __device__ __forceinline__ void operator()(bf16_t* tile, int row0) const {
+    if (row0 + 64 > nrows) {
+      tile_dma<D, NW>(tile, src, ld, row0, nrows, wave, lane);
+      return;
+    }
+    const char* base = reinterpret_cast<const char*>(src) + (int64_t)row0 * ld * 2;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const char* gp = base + (int64_t)u * NW * L::RG * ld * 2 + lane_off;
+      char* lp = reinterpret_cast<char*>(tile) + (wave + NW * u) * L::GS;
+      __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+    }
+  }
+};
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS byte address of a pointer into a __shared__ array.

@@ -39,11 +39,19 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int NW = 4>
+// NW waves in NG groups; each group owns all BM rows (32 per wave) and takes
+// every NG-th key tile (in-workgroup split over the keys when NG = 2).
+template <int D, int NW = 4, int NG = 1>
 struct FwdCfg {
-  static constexpr int BM = 32 * NW;       // query rows per workgroup (32 per wave)
+  static constexpr int WPG = NW / NG;      // waves per group
+  static constexpr int BM = 32 * WPG;      // query rows per workgroup (32 per wave)
   static constexpr int BN = kFwdBN;        // keys per tile
   static constexpr int NT = 64 * NW;       // threads
+  static constexpr int GT = 64 * WPG;      // threads per group
+  // Workgroups per CU the register budget is sized for: three 4-wave
+  // workgroups at D = 64 (at most 168 VGPRs, three waves per SIMD), else
+  // 8 waves per CU.
+  static constexpr int MINB = (D == 64 && NW == 4) ? 3 : 8 / NW;
   using L = TileLayout<D>;                 // LDS image of a 64-key K or V tile
   static constexpr int TB = L::BYTES;      // bytes per tile buffer
   static constexpr int DSTEPS = D / 16;
@@ -55,10 +63,6 @@ struct Tile {
   bool full;
 };
 
-template <typename V>
-__device__ __forceinline__ V zero_frag() {
-  return __builtin_bit_cast(V, make_uint4(0, 0, 0, 0));
-}
 
 struct TileCtx {
   float scale_log2;   // |scale| * log2(e)
@@ -211,12 +215,17 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
   }
 }
 
-// NW waves of 32 query rows: 4 (128 rows, two workgroups per CU) or 8 (256
-// rows, one workgroup per CU; each K/V tile copied to LDS feeds twice the
-// query rows, halving the L2-to-LDS traffic per flop).
-template <typename T, int D, int MOD, int NW>  // MOD bit 0: ALiBi, bit 1: softcap
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
-  using C = FwdCfg<D, NW>;
+// NW waves of 32 query rows: 4 (128 rows, two workgroups per CU), 8 in one
+// group (256 rows, one workgroup per CU; each K/V tile copied to LDS feeds
+// twice the query rows, halving the L2-to-LDS traffic per flop), or 8 in two
+// groups (NG = 2: 128 rows, the two groups take alternate key tiles and merge
+// their softmax states through LDS at the end).  With one workgroup per CU
+// the dispatcher hands out workgroups as CUs free up, so heaviest-first
+// order balances causal work; two 4-wave workgroups per CU are all placed at
+// once, pairing fixed tiles on a CU.
+template <typename T, int D, int MOD, int NW, int NG>  // MOD bit 0: ALiBi, bit 1: softcap
+__global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D, NW, NG>;
   constexpr bool kAlibi = MOD & 1;
   constexpr bool kSoftcap = MOD & 2;
 
@@ -224,18 +233,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // buffer): alias analysis can then see that the direct global->LDS copy of
   // the next tile does not touch the buffer being read, and no wait for the
   // copy is placed before the reads of the current tile.
-  __shared__ __attribute__((aligned(16))) char lds_k0[C::TB];
-  __shared__ __attribute__((aligned(16))) char lds_k1[C::TB];
-  __shared__ __attribute__((aligned(16))) char lds_v0[C::TB];
-  __shared__ __attribute__((aligned(16))) char lds_v1[C::TB];
-  __shared__ int lds_doc0[C::BN];
-  __shared__ int lds_doc1[C::BN];
+  // (One slice of TB bytes per group in each.)
+  __shared__ __attribute__((aligned(16))) char lds_k0_[NG * C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_k1_[NG * C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_v0_[NG * C::TB];
+  __shared__ __attribute__((aligned(16))) char lds_v1_[NG * C::TB];
+  __shared__ int lds_doc0_[NG * C::BN];
+  __shared__ int lds_doc1_[NG * C::BN];
 
-  const int tid = threadIdx.x;
+  const int tid_wg = threadIdx.x;
+  const int wave_wg = __builtin_amdgcn_readfirstlane(tid_wg >> 6);
+  const int grp = NG > 1 ? wave_wg / C::WPG : 0;  // key-tile group
+  const int tid = tid_wg - grp * C::GT;           // thread / wave index within the group
+  const int wave = wave_wg - grp * C::WPG;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;   // k-group of the MFMA operands
   const int c = lane & 31;   // column (query) of S^T / O^T
+  char* const lds_k0 = lds_k0_ + grp * C::TB;
+  char* const lds_k1 = lds_k1_ + grp * C::TB;
+  char* const lds_v0 = lds_v0_ + grp * C::TB;
+  char* const lds_v1 = lds_v1_ + grp * C::TB;
+  int* const lds_doc0 = lds_doc0_ + grp * C::BN;
+  int* const lds_doc1 = lds_doc1_ + grp * C::BN;
 
   // Heaviest query tiles first (causal work grows with the tile index); the
   // head index is permuted so that consecutive workgroups, which the
@@ -264,15 +283,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const float scale_abs = fabsf(a.scale);
   const uint32_t sign_flip = a.scale < 0.0f ? 0x80008000u : 0u;
   typename T::vec8 qf[C::DSTEPS];
+  uint4 raw[C::DSTEPS];
+  const int q_row = q_ok ? my_q : a.Sq - 1;
 #pragma unroll
   for (int ds = 0; ds < C::DSTEPS; ++ds) {
-    if (q_ok) {
-      uint4 raw = *reinterpret_cast<const uint4*>(qp + (int64_t)my_q * a.q_ss + 16 * ds + 8 * g);
-      raw.x ^= sign_flip; raw.y ^= sign_flip; raw.z ^= sign_flip; raw.w ^= sign_flip;
-      qf[ds] = __builtin_bit_cast(typename T::vec8, raw);
-    } else {
-      qf[ds] = zero_frag<typename T::vec8>();
-    }
+    // All loads first, unconditionally (a row past Sq reads row Sq - 1 and
+    // is zeroed below): loads guarded one by one were issued as a chain of
+    // round trips, each waited for before the next.
+    raw[ds] = *reinterpret_cast<const uint4*>(qp + (int64_t)q_row * a.q_ss + 16 * ds + 8 * g);
+  }
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    uint4 r = raw[ds];
+    r.x = q_ok ? r.x ^ sign_flip : 0u;
+    r.y = q_ok ? r.y ^ sign_flip : 0u;
+    r.z = q_ok ? r.z ^ sign_flip : 0u;
+    r.w = q_ok ? r.w ^ sign_flip : 0u;
+    qf[ds] = __builtin_bit_cast(typename T::vec8, r);
   }
 
   const float scale_log2 = scale_abs * kLog2e;
@@ -324,14 +351,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int delta = a.Sk - a.Sq;
 
   int doc_r = 0;
+  const TileCopy<D, C::WPG> kcopy(kp, a.k_ss, a.Sk, wave, lane);
+  const TileCopy<D, C::WPG> vcopy(vp, a.v_ss, a.Sk, wave, lane);
   // K and V of tile kt into buffer BUF (direct global->LDS), and this
   // thread's document id of the tile into a register.
   auto load_tile = [&](int kt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     char* kdst = BUF ? lds_k1 : lds_k0;
     char* vdst = BUF ? lds_v1 : lds_v0;
-    tile_dma<D, NW>(reinterpret_cast<bf16_t*>(kdst), kp, a.k_ss, kt * C::BN, a.Sk, wave, lane);
-    tile_dma<D, NW>(reinterpret_cast<bf16_t*>(vdst), vp, a.v_ss, kt * C::BN, a.Sk, wave, lane);
+    kcopy(reinterpret_cast<bf16_t*>(kdst), kt * C::BN);
+    vcopy(reinterpret_cast<bf16_t*>(vdst), kt * C::BN);
     if (has_doc && tid < C::BN) {
       const int key = kt * C::BN + tid;
       doc_r = key < a.Sk ? a.mask.doc_k[(int64_t)b * a.Sk + key] : -1;
@@ -356,8 +385,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
 
-  if (ntiles > 0) {
-    load_tile(tile_at(0).kt, B0{});
+  // Group grp takes tiles grp, grp + NG, ...: step s of the group is tile
+  // NG * s + grp.  Both groups run the same number of steps (one barrier
+  // each); a group past its last tile only takes part in the barriers.
+  if (grp < ntiles) {
+    load_tile(tile_at(grp).kt, B0{});
     store_doc(B0{});
   }
   wait_dma();
@@ -377,37 +409,81 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // is a compile-time choice, and full and partial tiles have loops of their
   // own, so each loop body is one instantiation and the accumulators keep
   // their registers across iterations.
-  auto step = [&](int t, auto buf_tag, auto masked) {
+  auto step = [&](int s, auto buf_tag, auto masked) {
     constexpr int BUF = decltype(buf_tag)::value;
     using NEXT = std::integral_constant<int, 1 - BUF>;
-    const Tile cur = tile_at(t);
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(tile_at(t + 1).kt, NEXT{});
-    if (trace_row != nullptr) {
-      if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
-      else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
+    const int t = NG * s + grp;
+    const bool has_next = t + NG < ntiles;
+    if (has_next) load_tile(tile_at(t + NG).kt, NEXT{});
+    if (NG == 1 || t < ntiles) {
+      const Tile cur = tile_at(t);
+      if (trace_row != nullptr) {
+        if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
+        else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
+      }
+      fwd_tile<T, D, MOD, decltype(masked)::value>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
+                                                BUF ? lds_doc1 : lds_doc0, qf, oacc, m_run, l_run,
+                                                ctx, cur.kt * C::BN, lane);
     }
-    fwd_tile<T, D, MOD, decltype(masked)::value>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
-                                              BUF ? lds_doc1 : lds_doc0, qf, oacc, m_run, l_run,
-                                              ctx, cur.kt * C::BN, lane);
     if (has_next) store_doc(NEXT{});
     wait_dma();
     __syncthreads();
   };
   using FULL = std::false_type;
   using PART = std::true_type;
+  // Steps of this group: nsteps in all, the first nfull_steps on FULL tiles.
+  const int nsteps = (ntiles + NG - 1) / NG;
+  const int nfull_steps = nfull_tiles > grp ? (nfull_tiles - grp + NG - 1) / NG : 0;
   int t = 0;
-  for (; t + 1 < nfull_tiles; t += 2) {
+  for (; t + 1 < nfull_steps; t += 2) {
     step(t, B0{}, FULL{});
     step(t + 1, B1{}, FULL{});
   }
-  if (t < nfull_tiles) step(t++, B0{}, FULL{});
-  if (t < ntiles && (t & 1)) step(t++, B1{}, PART{});
-  for (; t + 1 < ntiles; t += 2) {
+  if (t < nfull_steps) step(t++, B0{}, FULL{});
+  if (t < nsteps && (t & 1)) step(t++, B1{}, PART{});
+  for (; t + 1 < nsteps; t += 2) {
     step(t, B0{}, PART{});
     step(t + 1, B1{}, PART{});
   }
-  if (t < ntiles) step(t++, B0{}, PART{});
+  if (t < nsteps) step(t++, B0{}, PART{});
+
+  if constexpr (NG == 2) {
+    // Group 1 hands its running state (max, partial sums, unnormalised O)
+    // to group 0 through LDS (the tile buffers are free after the last
+    // step's barrier); wave w of each group owns the same 32 rows.
+    constexpr int SLOT = 64 * (16 * C::DBLK + 2);  // floats per wave
+    static_assert(SLOT * 4 <= C::TB, "state slot fits one tile buffer");
+    float* st = reinterpret_cast<float*>((wave < 2 ? lds_k0_ : lds_k1_) + (wave & 1) * C::TB);
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<float4*>(st + ((db * 4 + rr) * 64 + lane) * 4) =
+              make_float4(oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]);
+      st[16 * C::DBLK * 64 + lane] = m_run;
+      st[16 * C::DBLK * 64 + 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float mo = st[16 * C::DBLK * 64 + lane];
+    const float lo = st[16 * C::DBLK * 64 + 64 + lane];
+    const float M = fmaxf(m_run, mo);
+    const float a0 = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
+    const float a1 = mo == kNegInf ? 0.0f : fast_exp2(mo - M);
+    l_run = l_run * a0 + lo * a1;
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 x = *reinterpret_cast<const float4*>(st + ((db * 4 + rr) * 64 + lane) * 4);
+        oacc[db][4 * rr] = oacc[db][4 * rr] * a0 + x.x * a1;
+        oacc[db][4 * rr + 1] = oacc[db][4 * rr + 1] * a0 + x.y * a1;
+        oacc[db][4 * rr + 2] = oacc[db][4 * rr + 2] * a0 + x.z * a1;
+        oacc[db][4 * rr + 3] = oacc[db][4 * rr + 3] * a0 + x.w * a1;
+      }
+    m_run = M;
+  }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + wave_xor32(l_run);
@@ -431,17 +507,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int NG = 1>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
-  const int bm = 32 * NW;
+  const int bm = 32 * NW / NG;
   const int nqt = (a.Sq + bm - 1) / bm;
   const dim3 grid(nqt * a.Hq * a.B), block(64 * NW);
   const int mod = (a.alibi != nullptr ? 1 : 0) | (a.softcap > 0.0f ? 2 : 0);
   switch (mod) {
-    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 0, NW>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 1, NW>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 2, NW>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 3, NW>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 0, NW, NG>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 1, NW, NG>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 2, NW, NG>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<T, D, 3, NW, NG>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -458,16 +534,24 @@ int fwd_bf16_rows_per_block(int B, int Sq, int Hq, int causal, bool sparse) {
   return 128;
 }
 
+template <typename T, int D>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s, bool wide, bool split) {
+  if (wide) return launch_d<T, D, 8, 1>(a, s);
+  if (split) return launch_d<T, D, 8, 2>(a, s);
+  return launch_d<T, D, 4, 1>(a, s);
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
   if (a.Sq == 0 || a.B == 0 || a.Hq == 0) return hipSuccess;
   const bool sparse = a.tiles.kv_num_full != nullptr;
   const bool wide = fwd_bf16_rows_per_block(a.B, a.Sq, a.Hq, a.mask.causal, sparse) == 256;
-  if (a.f16) {
-    if (a.D == 64) return wide ? launch_d<F16T, 64, 8>(a, s) : launch_d<F16T, 64, 4>(a, s);
-    return wide ? launch_d<F16T, 128, 8>(a, s) : launch_d<F16T, 128, 4>(a, s);
-  }
-  if (a.D == 64) return wide ? launch_d<Bf16T, 64, 8>(a, s) : launch_d<Bf16T, 64, 4>(a, s);
-  return wide ? launch_d<Bf16T, 128, 8>(a, s) : launch_d<Bf16T, 128, 4>(a, s);
+  // 128-row tiles split over the keys in the workgroup when the grid is small
+  // (up to about 8 tiles per CU): placed two per CU, 4-wave workgroups would
+  // all be dispatched at once with fixed pairs of uneven causal tiles.
+  const long wg128 = (long)((a.Sq + 127) / 128) * a.Hq * a.B;
+  const bool split = !wide && !sparse && wg128 <= 2048;
+  if (a.f16) return a.D == 64 ? launch_t<F16T, 64>(a, s, wide, split) : launch_t<F16T, 128>(a, s, wide, split);
+  return a.D == 64 ? launch_t<Bf16T, 64>(a, s, wide, split) : launch_t<Bf16T, 128>(a, s, wide, split);
 }
 
 }  // namespace attn
