@@ -337,23 +337,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
 
   // K and V rows of this lane's key as B operands (d = 16*ds + 8*g .. +7).
   typename T::vec8 kf[C::DSTEPS], vf[C::DSTEPS];
-  // All loads are issued before any is used (a key past Sk reads key Sk - 1
-  // and is zeroed after): guarded one by one they became a chain of waited
-  // round trips.
-  {
-    const int key_row = k_ok ? my_key : a.Sk - 1;
-    uint4 kr[C::DSTEPS], vr[C::DSTEPS];
+  // (Guarded loads here: issuing all of them unconditionally, as the dQ
+  // kernel does, measured slower in this register-bound kernel.)
 #pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-      kr[ds] = *reinterpret_cast<const uint4*>(kp + (int64_t)key_row * a.k_ss + 16 * ds + 8 * g);
-      vr[ds] = *reinterpret_cast<const uint4*>(vp + (int64_t)key_row * a.v_ss + 16 * ds + 8 * g);
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+    if (k_ok) {
+      kr = *reinterpret_cast<const uint4*>(kp + (int64_t)my_key * a.k_ss + 16 * ds + 8 * g);
+      vr = *reinterpret_cast<const uint4*>(vp + (int64_t)my_key * a.v_ss + 16 * ds + 8 * g);
     }
-#pragma unroll
-    for (int ds = 0; ds < C::DSTEPS; ++ds) {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      kf[ds] = __builtin_bit_cast(typename T::vec8, k_ok ? kr[ds] : z);
-      vf[ds] = __builtin_bit_cast(typename T::vec8, k_ok ? vr[ds] : z);
-    }
+    kf[ds] = __builtin_bit_cast(typename T::vec8, kr);
+    vf[ds] = __builtin_bit_cast(typename T::vec8, vr);
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
 
@@ -397,14 +391,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   // is given, else lse2 again), so one counter value means "all but the
   // newest tile have landed".
   constexpr int kOpsPerTile = 2 * (64 / C::L::RG / 4) + 1;
-  const TileCopy<D> qcopy(qp, a.q_ss, a.Sq, wave, lane);
-  const TileCopy<D> docopy(dop, a.do_ss, a.Sq, wave, lane);
   auto load_tile = [&](int qt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
-    qcopy(reinterpret_cast<bf16_t*>(qd), qt * C::BM);
-    docopy(reinterpret_cast<bf16_t*>(dd), qt * C::BM);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(qd), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
+    tile_dma<D>(reinterpret_cast<bf16_t*>(dd), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
     // rows past Sq repeat the last row; they are masked on partial tiles
     const int i = min(qt * C::BM + lane, a.Sq - 1);
     const void* src;
