@@ -20,9 +20,13 @@
 //     32-query tiles of Q and dO through LDS.  S = Q K^T puts one key per
 //     lane, so P and dS (rounded to bf16) are directly the A operands of
 //     dV += P^T dO and dK += dS^T Q, whose B operands are transposed LDS
-//     reads of the dO and Q tiles.  With grouped-query heads each query head
-//     writes an fp32 partial and a reduction kernel sums the group in head
-//     order; with one query head per kv head the result is written directly.
+//     reads of the dO and Q tiles.  At D = 128 the deterministic schedule
+//     splits each 32-key block over two waves instead (2b): one holds K and
+//     produces P and dV, the other holds V and produces dS and dK, which
+//     halves the registers per wave so that two waves share each SIMD.
+//     With grouped-query heads each query head writes an fp32 partial and a
+//     reduction kernel sums the group in head order; with one query head per
+//     kv head the result is written directly.
 //  3. dQ: the forward's layout -- a workgroup owns 128 query rows, Q and dO
 //     stay in registers, K and V tiles stream through LDS; S^T = K Q^T and
 //     dP^T = V dO^T give one query per lane, and dQ^T += K^T dS^T uses
@@ -557,6 +561,399 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2b. dK / dV with paired waves (the deterministic schedule).
+//
+// The kernel above keeps K, V, dK and dV of 32 keys in one wave (over 400
+// registers), so one wave runs per SIMD and its matrix-core, vector and LDS
+// work serialise.  Here the four products of a 32-key block are split over
+// two waves of one workgroup (eight waves, 128 keys):
+//   wave A (waves 0-3) holds K:  S = Q K^T, P (masks, score mods), dV += P^T dO;
+//   wave B (waves 4-7) holds V:  dP = dO V^T, dS = P' (dP - Delta), dK += dS^T Q,
+// with P' = P (times 1 - tanh^2 under softcap) handed from A to B through LDS
+// in fp16 (P' lies in [0, 1], where fp16 keeps three more bits than bf16), one
+// tile later: at step t wave A works on query tile t
+// and wave B on tile t - 1, so the hand-over needs only the barrier that ends
+// each step.  Each wave holds about half the registers, so two run per SIMD,
+// and the LDS reads per tile are those of the single-wave kernel plus the
+// hand-over.
+
+template <int D>
+struct KVPairCfg {
+  static constexpr int NW = 8;
+  static constexpr int BN = 128;           // keys per workgroup (4 pairs x 32)
+  static constexpr int BM = 64;            // queries per streamed tile
+  using L = TileLayout<D>;
+  static constexpr int TB = L::BYTES;
+  static constexpr int DSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+  static constexpr int XB = 4096;          // one wave's P' tile: 32 keys x 64 queries x 2 bytes
+};
+
+// LDS offsets of the pair kernel's fragment reads, split into a per-lane part
+// (computed once) and a compile-time part (an instruction offset), so the
+// register allocator never holds one address per buffer and fragment.
+//   row read (A operand, row 32*qb + c, d = 16*ds + 8*g .. +7)
+//   transposed read (as tr_frag: 16-row step kk, 32-column block db; the
+//   second half of the fragment lies 8 rows further)
+template <int D>
+struct PairOff {
+  static constexpr int RG = TileLayout<D>::RG;
+  static constexpr int GS = TileLayout<D>::GS;
+  __device__ static int row_lane(int lane) {
+    const int g = lane >> 5, c = lane & 31;
+    return (c / RG) * GS + (g * RG + c % RG) * 16;
+  }
+  static constexpr int row(int qb, int ds) { return (32 * qb / RG) * GS + ds * 2 * RG * 16; }
+  __device__ static int tr_lane(int lane) {
+    const int beta = lane >> 4, s16 = lane & 15;
+    const int lr = 4 * (beta >> 1) + (s16 >> 2);
+    const int lc = 2 * (beta & 1) + ((s16 & 3) >> 1);
+    return (lr / RG) * GS + (lc * RG + lr % RG) * 16 + 8 * (s16 & 1);
+  }
+  static constexpr int tr(int kk, int db) { return (16 * kk / RG) * GS + db * 4 * RG * 16; }
+  static constexpr int TR_HI = (8 / RG) * GS;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ typename T::vec8 pair_row(const char* tile_lane, int qb, int ds) {
+  return *reinterpret_cast<const typename T::vec8*>(tile_lane + PairOff<D>::row(qb, ds));
+}
+template <typename T, int D>
+__device__ __forceinline__ typename T::vec8 pair_tr(const char* tile_lane, int kk, int db) {
+  const char* p = tile_lane + PairOff<D>::tr(kk, db);
+  return cat_frag<typename T::vec8>(lds_read_tr16(reinterpret_cast<const bf16_t*>(p)),
+                                    lds_read_tr16(reinterpret_cast<const bf16_t*>(p + PairOff<D>::TR_HI)));
+}
+
+// Wave A on one tile: S, P, the hand-over of P' and dV += P^T dO.
+template <typename T, int D, int MOD>
+__device__ __forceinline__ void pair_side_a(const char* qt_lds, const char* dot_lds, int lo_row, int lo_tr,
+                                            const float* lse_t,
+                                            const typename T::vec8 (&kf)[D / 16], f32x16 (&dv)[D / 32],
+                                            const BwdCtx& cx, int q0, int my_key, bool masked, int rows_first,
+                                            int rows_count, const int* docq_t, bool has_doc, int my_doc,
+                                            char* xb, int lane) {
+  using C = KVPairCfg<D>;
+  constexpr bool kAlibi = MOD & 1;
+  constexpr bool kSoftcap = MOD & 2;
+  const int g = lane >> 5, c = lane & 31;
+
+  f32x16 s[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    typename T::vec8 qa[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) qa[qb] = pair_row<T, D>(qt_lds + lo_row, qb, ds);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) s[qb] = mfma32(qa[qb], kf[ds], s[qb]);
+  }
+
+  typename T::vec8 pf[2][2];
+  f16x8 xh[2][2];  // P' for wave B, in fp16 whatever the input type (P' lies in [0, 1])
+  const uint32_t span = static_cast<uint32_t>(rows_count);
+  const int ib = q0 + 4 * g - rows_first;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qb + 8 * rr + 4 * g);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      int dv4[4] = {0, 0, 0, 0};
+      if (masked && has_doc) {
+        const int4 d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
+        dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rr + e;
+        float th = 0.0f;
+        const int i = q0 + roff(qb, r) + 4 * g;
+        float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[qb][r], lv[e], cx, i + cx.delta_pos - my_key, &th));
+        if (masked) {
+          // rows [rows_first, rows_first + rows_count) may see this key; with
+          // a document mask the row's document must also be the key's
+          bool ok = static_cast<uint32_t>(ib + roff(qb, r)) < span;
+          if (has_doc) ok = ok && dv4[e] == my_doc;
+          p = ok ? p : 0.0f;
+        }
+        pf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(p);
+        xh[qb][r >> 3][r & 7] = static_cast<_Float16>(kSoftcap ? p * (1.0f - th * th) : p);
+      }
+    }
+  // hand-over: chunk j = 2 qb + h of every lane at j * 1 KB + 16 * lane
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      *reinterpret_cast<f16x8*>(xb + (2 * qb + hh) * 1024 + 16 * lane) = xh[qb][hh];
+
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    typename T::vec8 fo[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) fo[db] = pair_tr<T, D>(dot_lds + lo_tr, kk, db);
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) dv[db] = mfma32(pf[kk >> 1][kk & 1], fo[db], dv[db]);
+  }
+}
+
+// Wave B on the previous tile: dP, dS from the handed-over P', dK += dS^T Q.
+template <typename T, int D>
+__device__ __forceinline__ void pair_side_b(const char* qt_lds, const char* dot_lds, int lo_row, int lo_tr,
+                                            const float* dl_t,
+                                            const typename T::vec8 (&vf)[D / 16], f32x16 (&dk)[D / 32],
+                                            const char* xb, int lane) {
+  using C = KVPairCfg<D>;
+  const int g = lane >> 5, c = lane & 31;
+
+  f32x16 dp[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp[qb][r] = 0.0f;
+#pragma unroll
+  for (int ds = 0; ds < C::DSTEPS; ++ds) {
+    typename T::vec8 da[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) da[qb] = pair_row<T, D>(dot_lds + lo_row, qb, ds);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma32(da[qb], vf[ds], dp[qb]);
+  }
+
+  f16x8 xh[2][2];
+  typename T::vec8 sf[2][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      xh[qb][hh] = *reinterpret_cast<const f16x8*>(xb + (2 * qb + hh) * 1024 + 16 * lane);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float4 d4 = *reinterpret_cast<const float4*>(dl_t + 32 * qb + 8 * rr + 4 * g);
+      const float dlv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rr + e;
+        const float pv = static_cast<float>(xh[qb][r >> 3][r & 7]);
+        sf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(pv * (dp[qb][r] - dlv[e]));
+      }
+    }
+
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    typename T::vec8 fq[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) fq[db] = pair_tr<T, D>(qt_lds + lo_tr, kk, db);
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) dk[db] = mfma32(sf[kk >> 1][kk & 1], fq[db], dk[db]);
+  }
+}
+
+template <typename T, int D, int MOD>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int partial) {
+  using C = KVPairCfg<D>;
+  // Three tile buffers (distinct LDS objects: a copy is never taken to alias
+  // the buffers being read): step t reads tiles t and t - 1 while t + 1 copies.
+  __shared__ __attribute__((aligned(16))) char lq0[C::TB];
+  __shared__ __attribute__((aligned(16))) char lq1[C::TB];
+  __shared__ __attribute__((aligned(16))) char lq2[C::TB];
+  __shared__ __attribute__((aligned(16))) char ld0[C::TB];
+  __shared__ __attribute__((aligned(16))) char ld1[C::TB];
+  __shared__ __attribute__((aligned(16))) char ld2[C::TB];
+  __shared__ __attribute__((aligned(16))) float ll0[C::BM];
+  __shared__ __attribute__((aligned(16))) float ll1[C::BM];
+  __shared__ __attribute__((aligned(16))) float ll2[C::BM];
+  __shared__ __attribute__((aligned(16))) float lg0[C::BM];
+  __shared__ __attribute__((aligned(16))) float lg1[C::BM];
+  __shared__ __attribute__((aligned(16))) float lg2[C::BM];
+  __shared__ __attribute__((aligned(16))) int lz0[C::BM];
+  __shared__ __attribute__((aligned(16))) int lz1[C::BM];
+  __shared__ __attribute__((aligned(16))) int lz2[C::BM];
+  __shared__ __attribute__((aligned(16))) char lx[2 * 4 * C::XB];  // P' hand-over, by step parity and pair
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool side_a = wave < 4;
+  const int pair = wave & 3;
+  const int lo_row = PairOff<D>::row_lane(lane), lo_tr = PairOff<D>::tr_lane(lane);
+  const int g = lane >> 5, c = lane & 31;
+  const int per = a.Hq * a.B;
+  const int kt = blockIdx.x / per;  // key tiles near the start see the most causal rows
+  const int rem = blockIdx.x % per;
+  const int b = rem / a.Hq;
+  int h = rem % a.Hq;
+  if ((a.Hq & 7) == 0) h = (h & 7) * (a.Hq >> 3) + (h >> 3);
+  const int Gq = a.Hq / a.Hkv;
+  const int kvh = h / Gq;
+
+  const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
+  const bf16_t* dop = static_cast<const bf16_t*>(a.dout) + b * a.do_sb + h * a.do_sh;
+  const float* lsep = a.lse2 + ((int64_t)b * a.Hq + h) * a.Sq;
+  const float* dlp = a.delta + ((int64_t)b * a.Hq + h) * a.Sq;
+
+  const int kv0 = kt * C::BN + 32 * pair;  // the pair's first key
+  const int my_key = kv0 + c;
+  const bool k_ok = my_key < a.Sk;
+
+  // K (wave A) or V (wave B) of this lane's key as B operands, d = 16*ds + 8*g .. +7.
+  typename T::vec8 xf[C::DSTEPS];
+  {
+    const bf16_t* src = side_a ? static_cast<const bf16_t*>(a.k) + b * a.k_sb + kvh * a.k_sh
+                               : static_cast<const bf16_t*>(a.v) + b * a.v_sb + kvh * a.v_sh;
+    const int64_t ld = side_a ? a.k_ss : a.v_ss;
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (k_ok) x = *reinterpret_cast<const uint4*>(src + (int64_t)my_key * ld + 16 * ds + 8 * g);
+      xf[ds] = __builtin_bit_cast(typename T::vec8, x);
+    }
+  }
+  const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
+
+  // Query tiles that meet the workgroup's keys (as in the kernel above).
+  const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
+  constexpr bool sparse = (MOD & 4) != 0;
+  int qt_begin = 0, ntiles = 0, n_full_blk = 0;
+  const int32_t* qi_full = nullptr;
+  const int32_t* qi_part = nullptr;
+  if (sparse) {
+    const int u = b * a.tiles.nK + (kt * C::BN) / a.tiles.block_n;
+    n_full_blk = a.tiles.q_num_full[u];
+    ntiles = 2 * (n_full_blk + a.tiles.q_num_partial[u]);
+    qi_full = a.tiles.q_idx_full + (int64_t)u * a.tiles.nQ;
+    qi_part = a.tiles.q_idx_partial + (int64_t)u * a.tiles.nQ;
+  } else {
+    const int c0 = kt * C::BN, c1 = min(a.Sk, c0 + C::BN) - 1;
+    int i_lo = 0, i_hi = a.Sq - 1;
+    if (win.R != kUnbounded) i_lo = max(i_lo, c0 - cx.delta_pos - win.R);
+    if (win.L != kUnbounded) i_hi = min(i_hi, c1 - cx.delta_pos + win.L);
+    qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
+    ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
+  }
+  auto qt_of = [&](int t) -> int {
+    if (!sparse) return qt_begin + t;
+    const int blk = t >> 1;
+    return 2 * (blk < n_full_blk ? qi_full[blk] : qi_part[blk - n_full_blk]) + (t & 1);
+  };
+  // Whether this pair's 32 keys meet query tile t, and whether a predicate is needed.
+  auto tile_state = [&](int t, int qt, bool* masked) -> bool {
+    if (sparse) {
+      *masked = (t >> 1) >= n_full_blk;
+      return true;
+    }
+    const TileRange trq(win, qt, C::BM, 32);
+    const int kw = kv0 / 32;
+    *masked = !trq.full(kw);
+    return kw >= trq.kt_begin && kw < trq.kt_end;
+  };
+  int rows_first, rows_count;
+  win.key_rows(my_key, &rows_first, &rows_count);
+  const bool has_doc = sparse && a.mask.doc_q != nullptr;
+  const int my_doc = has_doc && k_ok ? a.mask.doc_k[(int64_t)b * a.Sk + my_key] : 0;
+  const int32_t* docq = has_doc ? a.mask.doc_q + (int64_t)b * a.Sq : nullptr;
+
+  // Copies of one tile: every wave its share of the Q and dO rows; waves 0,
+  // 1 and 2 (with a document mask) one 64-entry row of lse2, Delta and the
+  // rows' document ids.  Rows past Sq repeat the last row (masked by wave A,
+  // and their P' is zero for wave B).
+  auto load_tile = [&](int qt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
+    char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
+    tile_dma<D, C::NW>(reinterpret_cast<bf16_t*>(qd), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
+    tile_dma<D, C::NW>(reinterpret_cast<bf16_t*>(dd), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
+    const int i = min(qt * C::BM + lane, a.Sq - 1);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(lsep + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2)), 4, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_global_load_lds(dlp + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2)), 4, 0, 0);
+    else if (wave == 2 && has_doc)
+      __builtin_amdgcn_global_load_lds(docq + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2)), 4, 0, 0);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+
+  f32x16 acc[C::DBLK];  // dV (wave A) or dK (wave B)
+#pragma unroll
+  for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  if (ntiles > 0) load_tile(qt_of(0), B0{});
+  wait_dma();
+  __syncthreads();
+
+  // Step t (BUF = t mod 3): wave A on tile t, wave B on tile t - 1, the copy
+  // of tile t + 1 in flight.
+  auto step = [&](int t, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    using NEXT = std::integral_constant<int, (BUF + 1) % 3>;
+    constexpr int PREV = (BUF + 2) % 3;
+    if (t + 1 < ntiles) load_tile(qt_of(t + 1), NEXT{});
+    if (side_a) {
+      if (t < ntiles) {
+        const int qt = qt_of(t);
+        bool masked;
+        if (tile_state(t, qt, &masked))
+          pair_side_a<T, D, MOD>(BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2), BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2),
+                                 lo_row, lo_tr, BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2), xf, acc, cx, qt * C::BM, my_key, masked,
+                                 rows_first, rows_count, BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2), has_doc, my_doc,
+                                 lx + ((t & 1) * 4 + pair) * C::XB, lane);
+      }
+    } else if (t >= 1) {
+      const int qt = qt_of(t - 1);
+      bool masked;
+      if (tile_state(t - 1, qt, &masked))
+        pair_side_b<T, D>(PREV == 0 ? lq0 : (PREV == 1 ? lq1 : lq2), PREV == 0 ? ld0 : (PREV == 1 ? ld1 : ld2),
+                          lo_row, lo_tr, PREV == 0 ? lg0 : (PREV == 1 ? lg1 : lg2), xf, acc,
+                          lx + (((t - 1) & 1) * 4 + pair) * C::XB, lane);
+    }
+    wait_dma();       // tile t + 1 has landed ...
+    __syncthreads();  // ... for every wave, and P'(t) is visible to wave B
+  };
+  const int nsteps = ntiles > 0 ? ntiles + 1 : 0;
+  int t = 0;
+  for (; t + 2 < nsteps; t += 3) {
+    step(t, B0{});
+    step(t + 1, B1{});
+    step(t + 2, B2{});
+  }
+  if (t < nsteps) step(t++, B0{});
+  if (t < nsteps) step(t++, B1{});
+
+  // acc[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c; wave A holds
+  // dV, wave B dK (scaled here).
+  const float mul = side_a ? 1.0f : a.scale;
+#pragma unroll
+  for (int db = 0; db < C::DBLK; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (key >= a.Sk) continue;
+      const int d = 32 * db + c;
+      const float val = acc[db][r] * mul;
+      if (partial) {
+        const int64_t idx = (((int64_t)b * a.Sk + key) * a.Hq + h) * D + d;
+        (side_a ? a.part_dv : a.part_dk)[idx] = val;
+      } else if (side_a) {
+        bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)key * a.dv_ss + kvh * a.dv_sh;
+        dvp[d] = f32_to_elem<T>(val);
+      } else {
+        bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)key * a.dk_ss + kvh * a.dk_sh;
+        dkp[d] = f32_to_elem<T>(val);
+      }
+    }
+  }
+}
+
 // Sum the G per-head partials of each kv head in head order -> bf16.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs a) {
@@ -848,11 +1245,17 @@ template <typename T, int D, int MOD>
 hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int partial = G > 1 ? 1 : 0;
+  static_assert(KVPairCfg<D>::BN == KVCfg<D>::BN, "both dK/dV kernels take 128 keys per workgroup");
   const int nkt = (a.Sk + KVCfg<D>::BN - 1) / KVCfg<D>::BN;
   const bool atomic_dq = a.dq_acc != nullptr;
   if ((stages & 2) && nkt > 0) {
+    // Paired waves at D = 128; at D = 64 a tile has half the matrix work
+    // against the same softmax work, so wave A's vector ALU sets the pace
+    // and the single-wave kernel measured faster.
     if (atomic_dq)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, true>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
+    else if constexpr (D == 128)
+      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, MOD>), dim3(nkt * a.Hq * a.B), dim3(512), 0, s, a, partial);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
     hipError_t e = hipGetLastError();

@@ -194,7 +194,9 @@ attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype,
  *             without atomics (a separate dQ pass), so repeated calls are
  *             bitwise identical.  0 = dQ is accumulated by the dK/dV pass
  *             with fp32 atomic adds into the workspace and then scaled and
- *             rounded (FA's non-deterministic schedule; dK, dV unchanged).
+ *             rounded (FA's non-deterministic schedule).  dK and dV take no
+ *             atomics in either schedule; at D = 128 their kernels differ,
+ *             so dK of 0 and 1 agree to rounding, not bitwise.
  *             On gfx950 fp32 device atomics sustain only a few hundred G
  *             adds/s, so 0 is the slower schedule here (about 4x on
  *             B1 H32/8 S2048 D128 causal); 1 is the fast path.

@@ -206,8 +206,9 @@ def test_bwd_nondeterministic_block_sparse(b):
 
 def test_bwd_nondeterministic_llama8b_full(b):
     """The B=1, Hq=32, Hkv=8, S=2048, D=128 causal workload with atomic dQ:
-    every gradient element against the oracle; dK and dV, which take no
-    atomics, are bitwise those of the deterministic schedule."""
+    every gradient element against the oracle, and dV and dQ against the
+    deterministic schedule (whose dK/dV kernel at D = 128 forms dS from P
+    handed between two waves in fp16, so its dK differs in rounding)."""
     w = inputs.llama8b_train()
     kw = dict(softmax_scale=w["scale"], causal=True)
     dq, dk, dv = run_bwd_nd(b, w, {}, **kw)
@@ -216,7 +217,10 @@ def test_bwd_nondeterministic_llama8b_full(b):
     check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
     check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
     dq1, dk1, dv1 = run_bwd(b, w, **kw)
-    assert torch.equal(dk, dk1) and torch.equal(dv, dv1)
+    assert torch.equal(dv, dv1)
+    # dV comes from the same arithmetic in both schedules; dK of each is held
+    # to the oracle above (its dS roundings differ, and dK sums cancelling
+    # terms, so no tighter bound between the two holds by construction)
     assert float((dq.float() - dq1.float()).abs().max()) <= 1e-2
 
 
