@@ -954,28 +954,49 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   }
 }
 
-// Sum the G per-head partials of each kv head in head order -> bf16.
+// Sum the G per-head partials of each kv head in head order -> bf16.  One
+// thread per 8 consecutive d of one (b, key, kv head): 16-byte loads of each
+// head's partials and one 16-byte store per output.  Row indices fit 32 bits
+// (the fp32 partials of B*Sk*Hq rows of D floats must fit device memory).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(BwdArgs a) {
-  const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * D;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n) return;
-  const int d = static_cast<int>(t % D);
-  const int g = static_cast<int>((t / D) % a.Hkv);
-  const int64_t bj = t / ((int64_t)D * a.Hkv);
+  constexpr int CH = D / 8;  // 8-element chunks per row
+  const uint32_t rows = static_cast<uint32_t>(a.B) * a.Sk * a.Hkv;
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if ((uint64_t)t >= (uint64_t)rows * CH) return;
+  const int ch = static_cast<int>(t % CH);
+  const uint32_t row = t / CH;  // (b * Sk + j) * Hkv + g
+  const int g = static_cast<int>(row % a.Hkv);
+  const uint32_t bj = row / a.Hkv;
   const int j = static_cast<int>(bj % a.Sk);
   const int b = static_cast<int>(bj / a.Sk);
   const int G = a.Hq / a.Hkv;
-  const int64_t base = (((int64_t)b * a.Sk + j) * a.Hq + (int64_t)g * G) * D + d;
-  float sk = 0.0f, sv = 0.0f;
+  const int64_t base = ((int64_t)bj * a.Hq + (int64_t)g * G) * D + 8 * ch;
+  float sk[8], sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.0f;
   for (int x = 0; x < G; ++x) {
-    sk += a.part_dk[base + (int64_t)x * D];
-    sv += a.part_dv[base + (int64_t)x * D];
+    const float4* pk = reinterpret_cast<const float4*>(a.part_dk + base + (int64_t)x * D);
+    const float4* pv = reinterpret_cast<const float4*>(a.part_dv + base + (int64_t)x * D);
+    const float4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+    const float kx[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    const float vx[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sk[e] += kx[e];
+      sv[e] += vx[e];
+    }
   }
-  bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)j * a.dk_ss + g * a.dk_sh;
-  bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)j * a.dv_ss + g * a.dv_sh;
-  dkp[d] = f32_to_elem<T>(sk);
-  dvp[d] = f32_to_elem<T>(sv);
+  uint32_t wk[4], wv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    wk[e] = f32_to_elem<T>(sk[2 * e]) | (uint32_t)f32_to_elem<T>(sk[2 * e + 1]) << 16;
+    wv[e] = f32_to_elem<T>(sv[2 * e]) | (uint32_t)f32_to_elem<T>(sv[2 * e + 1]) << 16;
+  }
+  bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)j * a.dk_ss + g * a.dk_sh + 8 * ch;
+  bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)j * a.dv_ss + g * a.dv_sh + 8 * ch;
+  *reinterpret_cast<uint4*>(dkp) = make_uint4(wk[0], wk[1], wk[2], wk[3]);
+  *reinterpret_cast<uint4*>(dvp) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
 }
 
 // Non-deterministic dQ: scale the fp32 accumulator and round to bf16.
@@ -1262,7 +1283,7 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 4) && partial && a.Sk > 0) {
-    const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * D;
+    const int64_t n = (int64_t)a.B * a.Sk * a.Hkv * (D / 8);
     hipLaunchKernelGGL((bwd_group_sum_kernel<T, D>), dim3((n + 255) / 256), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
