@@ -332,14 +332,17 @@ def attn_bwd_kvpacked(q, kv, out, dout, lse, softmax_scale=None, causal=False, w
 
 
 def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softmax_scale=None,
-                   causal=False, window=(-1, -1), alibi_slopes=None, softcap=0.0, block_mask=None):
-    """Enqueue one stage (0 Delta, 1 dK/dV, 2 group sum, 3 dQ) of attn_bwd;
-    stages 0..3 in order with one workspace equal attn_bwd."""
+                   causal=False, window=(-1, -1), alibi_slopes=None, softcap=0.0, block_mask=None,
+                   deterministic=True):
+    """Enqueue one stage of attn_bwd (deterministic: 0 dQ with Delta, 1 dK/dV,
+    2 group sum, 3 nothing; see attn.h); stages 0..3 in order with one
+    workspace equal attn_bwd."""
     D = q.shape[3]
     p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask)
     _check(_lib.attn_bwd_stage(ctypes.byref(p), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
-                               _tensor(dout), _ptr(lse), _tensor(dq), _tensor(dk), _tensor(dv), 1,
-                               _ptr(workspace), workspace.numel(), int(stage), _stream()))
+                               _tensor(dout), _ptr(lse), _tensor(dq), _tensor(dk), _tensor(dv),
+                               1 if deterministic else 0, _ptr(workspace), workspace.numel(),
+                               int(stage), _stream()))
 
 
 def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=0.0,

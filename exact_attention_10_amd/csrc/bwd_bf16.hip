@@ -12,9 +12,12 @@
 //   dK  += scale * dS^T Q
 //   dQ  += scale * dS K
 //
-// Three kernels, no atomics (every output element is summed in a fixed
-// order, so results are bitwise repeatable):
-//  1. preprocess: Delta_i = <dO_i, O_i> in fp32.
+// Kernels of the deterministic schedule, no atomics (every output element is
+// summed in a fixed order, so results are bitwise repeatable), in launch
+// order: dQ (which also forms Delta_i = <dO_i, O_i> in fp32 and the LSE in
+// exp2 units for its rows), dK/dV, and for GQA the group sum.  The atomic-dQ
+// schedule runs a separate Delta pass (1) first.
+//  1. preprocess (atomic-dQ schedule): Delta and lse2, zeroed dQ accumulator.
 //  2. dK/dV: a workgroup owns 128 keys of one (batch, query head); each wave
 //     keeps its 32 keys of K and V in registers as MFMA operands and streams
 //     32-query tiles of Q and dO through LDS.  S = Q K^T puts one key per
@@ -30,7 +33,8 @@
 //  3. dQ: the forward's layout -- a workgroup owns 128 query rows, Q and dO
 //     stay in registers, K and V tiles stream through LDS; S^T = K Q^T and
 //     dP^T = V dO^T give one query per lane, and dQ^T += K^T dS^T uses
-//     transposed reads of the K tile.
+//     transposed reads of the K tile.  Each lane holds half of its row's dO,
+//     so Delta is its half of <dO, O> plus the partner lane's.
 
 #include <type_traits>
 
@@ -1139,12 +1143,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // (All loads issued before any use; rows past Sq read row Sq - 1 and are
   // zeroed after.)
   const int q_row = q_ok ? my_q : a.Sq - 1;
+  const int64_t row_idx = ((int64_t)b * a.Hq + h) * a.Sq + q_row;
+  float d_part = 0.0f;  // this lane's half of Delta = <dO, O> (d = 16*ds + 8*g .. +7)
   {
-    uint4 r1[C::DSTEPS], r2[C::DSTEPS];
+    const bf16_t* op = static_cast<const bf16_t*>(a.o) + b * a.o_sb + h * a.o_sh;
+    uint4 r1[C::DSTEPS], r2[C::DSTEPS], r3[C::DSTEPS];
 #pragma unroll
     for (int ds = 0; ds < C::DSTEPS; ++ds) {
       r1[ds] = *reinterpret_cast<const uint4*>(qp + (int64_t)q_row * a.q_ss + 16 * ds + 8 * g);
       r2[ds] = *reinterpret_cast<const uint4*>(dop + (int64_t)q_row * a.do_ss + 16 * ds + 8 * g);
+      r3[ds] = *reinterpret_cast<const uint4*>(op + (int64_t)q_row * a.o_ss + 16 * ds + 8 * g);
+    }
+#pragma unroll
+    for (int ds = 0; ds < C::DSTEPS; ++ds) {
+      const uint32_t dw[4] = {r2[ds].x, r2[ds].y, r2[ds].z, r2[ds].w};
+      const uint32_t ow[4] = {r3[ds].x, r3[ds].y, r3[ds].z, r3[ds].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d_part = __builtin_fmaf(T::to_f32(dw[e] & 0xffffu), T::to_f32(ow[e] & 0xffffu), d_part);
+        d_part = __builtin_fmaf(T::to_f32(dw[e] >> 16), T::to_f32(ow[e] >> 16), d_part);
+      }
     }
 #pragma unroll
     for (int ds = 0; ds < C::DSTEPS; ++ds) {
@@ -1154,10 +1172,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
   const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
-  const float l_row = a.lse[((int64_t)b * a.Hq + h) * a.Sq + q_row];
-  const float d_row = a.delta[((int64_t)b * a.Hq + h) * a.Sq + q_row];
-  const float lse2 = !q_ok || l_row == kNegInf ? kPosInf : l_row * kLog2e;
+  const float l_row = a.lse[row_idx];
+  const float lse2 = !q_ok || l_row == kNegInf ? kPosInf : l_row * kLog2e;  // empty rows: P = 0
+  const float d_row = d_part + wave_xor32(d_part);
   const float dl = q_ok ? d_row : 0.0f;
+  // Delta and lse2 of every row for the dK/dV kernel, which runs after this
+  // one (written before any early exit: it reads them for every row it meets).
+  if (q_ok && g == 0) {
+    a.delta[row_idx] = d_row;
+    a.lse2[row_idx] = lse2;
+  }
 
   // Key tiles in processing order, FULL ones first.  Dense: the interval of
   // the causal / window band.  Block-sparse: the mask's FULL then PARTIAL
@@ -1269,6 +1293,14 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   static_assert(KVPairCfg<D>::BN == KVCfg<D>::BN, "both dK/dV kernels take 128 keys per workgroup");
   const int nkt = (a.Sk + KVCfg<D>::BN - 1) / KVCfg<D>::BN;
   const bool atomic_dq = a.dq_acc != nullptr;
+  // Deterministic schedule: stage 0 is the dQ kernel, which also writes
+  // Delta and lse2 for the dK/dV kernel (no separate Delta pass).
+  const int nqt0 = (a.Sq + QCfg<D>::BM - 1) / QCfg<D>::BM;
+  if ((stages & 1) && !atomic_dq && nqt0 > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MOD>), dim3(nqt0 * a.Hq * a.B), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if ((stages & 2) && nkt > 0) {
     // Paired waves at D = 128; at D = 64 a tile has half the matrix work
     // against the same softmax work, so wave A's vector ALU sets the pace
@@ -1289,21 +1321,19 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int nqt = (a.Sq + QCfg<D>::BM - 1) / QCfg<D>::BM;
-  if (!(stages & 8) || nqt == 0) return hipSuccess;
-  if (atomic_dq) {
+  if ((stages & 8) && atomic_dq && nqt > 0) {
     const int64_t n = (int64_t)a.B * a.Sq * a.Hq * (D / 8);
     hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), dim3((n + 255) / 256), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MOD>), dim3(nqt * a.Hq * a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <typename T, int D>
 hipError_t launch_d(const BwdArgs& a, int stages, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.Sq * a.Hq;
   constexpr int LPR = D / 8;
-  if ((stages & 1) && rows > 0) {
+  if ((stages & 1) && rows > 0 && a.dq_acc != nullptr) {  // the atomic-dQ schedule's Delta pass
     hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((rows * LPR + 255) / 256), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -223,14 +223,17 @@ size_t attn_bwd_workspace_size(const attn_params* p);
 /* One stage of attn_bwd, same arguments and workspace, for callers that
  * time or interleave the stages.  Enqueuing stages 0, 1, 2, 3 in order on one
  * stream (with the same workspace) is exactly attn_bwd:
- *   0  Delta_i = <dout_i, o_i> into the workspace
- *   1  dK/dV kernel (fp32 per-head partials in the workspace when Hq > Hkv,
- *      else dk/dv directly; with deterministic == 0 also the atomic dQ
- *      accumulation, which stage 0 zeroes)
+ *   0  deterministic == 1: the dQ kernel, which also writes
+ *      Delta_i = <dout_i, o_i> and the LSE in exp2 units into the workspace;
+ *      deterministic == 0: Delta and the LSE alone, and zeroes the dQ
+ *      accumulator
+ *   1  dK/dV kernel, reading Delta (fp32 per-head partials in the workspace
+ *      when Hq > Hkv, else dk/dv directly; with deterministic == 0 also the
+ *      atomic dQ accumulation)
  *   2  sum of the per-head partials of each kv head into dk/dv, in head order
  *      (nothing to do when Hq == Hkv)
- *   3  dQ kernel (reads Delta); with deterministic == 0 the scale-and-round
- *      of the dQ accumulator
+ *   3  deterministic == 0: the scale-and-round of the dQ accumulator;
+ *      nothing to do for deterministic == 1
  * Errors: as attn_bwd; INVALID_ARG for a stage outside 0..3. */
 attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
                            attn_tensor v, attn_tensor o, attn_tensor dout,

@@ -265,3 +265,23 @@ def test_kvpacked_gqa(b):
                                       causal=True)
     check_o(to_f64(dkv[:, :, 0]), rk, GRAD_ATOL, "dK")
     check_o(to_f64(dkv[:, :, 1]), rv, GRAD_ATOL, "dV")
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+@pytest.mark.parametrize("case", [CASES[i] for i in (1, 3)], ids=["1", "3"])
+def test_bwd_stages_equal_attn_bwd(b, case, deterministic):
+    """attn_bwd_stage 0, 1, 2, 3 in order on one stream and workspace give
+    exactly attn_bwd's gradients (either schedule; GQA and ragged shapes)."""
+    B, Sq, Sk, Hq, Hkv, D, opt = case
+    w = inputs.random_case(500 + Sq + D, B, Sq, Sk, Hq, Hkv, D, dtype="bf16", grad=True)
+    kw = dict(softmax_scale=0.11, causal=opt.get("causal", False))
+    q, k, v, do = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v", "do"))
+    o, lse = b.attn_fwd(q, k, v, **kw)
+    ref = b.attn_bwd(q, k, v, o, do, lse, deterministic=deterministic, **kw)
+    ws = torch.empty(b.bwd_workspace_size(q, k), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for st in range(4):
+        b.attn_bwd_stage(st, q, k, v, o, do, lse, dq, dk, dv, ws, deterministic=deterministic, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip((dq, dk, dv), ref):
+        assert torch.equal(x, y)
