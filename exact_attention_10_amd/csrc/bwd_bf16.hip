@@ -745,8 +745,11 @@ __device__ __forceinline__ void pair_side_b(const char* qt_lds, const char* dot_
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * rr + e;
+        // written as an fma with a zero addend so the fp16 operand is read
+        // by one mixed-precision fma (no separate conversion); it differs
+        // from the product only in the sign of a zero result
         const float pv = static_cast<float>(xh[qb][r >> 3][r & 7]);
-        sf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(pv * (dp[qb][r] - dlv[e]));
+        sf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(__builtin_fmaf(pv, dp[qb][r] - dlv[e], 0.0f));
       }
     }
 
@@ -841,13 +844,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
     qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
     ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
   }
-  auto qt_of = [&](int t) -> int {
+  auto qt_of = [&](int t) __attribute__((always_inline)) -> int {
     if (!sparse) return qt_begin + t;
     const int blk = t >> 1;
     return 2 * (blk < n_full_blk ? qi_full[blk] : qi_part[blk - n_full_blk]) + (t & 1);
   };
   // Whether this pair's 32 keys meet query tile t, and whether a predicate is needed.
-  auto tile_state = [&](int t, int qt, bool* masked) -> bool {
+  auto tile_state = [&](int t, int qt, bool* masked) __attribute__((always_inline)) -> bool {
     if (sparse) {
       *masked = (t >> 1) >= n_full_blk;
       return true;
@@ -867,12 +870,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   // 1 and 2 (with a document mask) one 64-entry row of lse2, Delta and the
   // rows' document ids.  Rows past Sq repeat the last row (masked by wave A,
   // and their P' is zero for wave B).
-  auto load_tile = [&](int qt, auto buf_tag) {
+  const TileCopy<D, C::NW> qcopy(qp, a.q_ss, a.Sq, wave, lane);
+  const TileCopy<D, C::NW> dcopy(dop, a.do_ss, a.Sq, wave, lane);
+  auto load_tile = [&](int qt, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
-    tile_dma<D, C::NW>(reinterpret_cast<bf16_t*>(qd), qp, a.q_ss, qt * C::BM, a.Sq, wave, lane);
-    tile_dma<D, C::NW>(reinterpret_cast<bf16_t*>(dd), dop, a.do_ss, qt * C::BM, a.Sq, wave, lane);
+    qcopy(reinterpret_cast<bf16_t*>(qd), qt * C::BM);
+    dcopy(reinterpret_cast<bf16_t*>(dd), qt * C::BM);
     const int i = min(qt * C::BM + lane, a.Sq - 1);
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(lsep + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2)), 4, 0, 0);
@@ -896,13 +901,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   __syncthreads();
 
   // Step t (BUF = t mod 3): wave A on tile t, wave B on tile t - 1, the copy
-  // of tile t + 1 in flight.
-  auto step = [&](int t, auto buf_tag) {
+  // of tile t + 1 in flight.  The role is a compile-time tag and each role
+  // runs its own copy of the loop (the same steps and barriers), so the
+  // accumulators never meet a branch join inside the loop (a join made the
+  // compiler copy them every step).
+  auto step = [&](int t, auto buf_tag, auto role_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool kA = decltype(role_tag)::value;
     using NEXT = std::integral_constant<int, (BUF + 1) % 3>;
     constexpr int PREV = (BUF + 2) % 3;
     if (t + 1 < ntiles) load_tile(qt_of(t + 1), NEXT{});
-    if (side_a) {
+    if constexpr (kA) {
       if (t < ntiles) {
         const int qt = qt_of(t);
         bool masked;
@@ -924,14 +933,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
     __syncthreads();  // ... for every wave, and P'(t) is visible to wave B
   };
   const int nsteps = ntiles > 0 ? ntiles + 1 : 0;
-  int t = 0;
-  for (; t + 2 < nsteps; t += 3) {
-    step(t, B0{});
-    step(t + 1, B1{});
-    step(t + 2, B2{});
-  }
-  if (t < nsteps) step(t++, B0{});
-  if (t < nsteps) step(t++, B1{});
+  auto run = [&](auto role_tag) __attribute__((always_inline)) {
+    int t = 0;
+    for (; t + 2 < nsteps; t += 3) {
+      step(t, B0{}, role_tag);
+      step(t + 1, B1{}, role_tag);
+      step(t + 2, B2{}, role_tag);
+    }
+    if (t < nsteps) step(t++, B0{}, role_tag);
+    if (t < nsteps) step(t++, B1{}, role_tag);
+  };
+  if (side_a)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // acc[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c; wave A holds
   // dV, wave B dK (scaled here).
