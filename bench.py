@@ -238,6 +238,9 @@ def main():
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "kernels": kernels,
+        # SHA-256 of the bf16 bytes of each seeded input as uploaded
+        "inputs_sha256": {n: hashlib.sha256(np.ascontiguousarray(w[n]).tobytes()).hexdigest()
+                          for n in ("q", "k", "v", "do")},
     }
 
     # the same backward with deterministic=0 (dQ by fp32 atomic adds in the
