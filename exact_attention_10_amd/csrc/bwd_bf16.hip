@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
     ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
   }
-  auto qt_of = [&](int t) -> int {
+  auto qt_of = [&](int t) __attribute__((always_inline)) -> int {
     if (!sparse) return qt_begin + t;
     const int blk = t >> 1;
     return 2 * (blk < n_full_blk ? qi_full[blk] : qi_part[blk - n_full_blk]) + (t & 1);
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   // is given, else lse2 again), so one counter value means "all but the
   // newest tile have landed".
   constexpr int kOpsPerTile = 2 * (64 / C::L::RG / 4) + 1;
-  auto load_tile = [&](int qt, auto buf_tag) {
+  auto load_tile = [&](int qt, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     }
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
   };
-  auto wait_older = [&](bool newest_in_flight) {
+  auto wait_older = [&](bool newest_in_flight) __attribute__((always_inline)) {
     if (newest_in_flight) {
       if constexpr (kOpsPerTile == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   // query block w % 2 and D/64 of the 32-column blocks; fp32 atomic adds
   // into the accumulator (rows past Sq skipped; their dS is zero anyway).
   float* dq_row0 = kDq ? a.dq_acc + ((int64_t)b * a.Sq * a.Hq + h) * D : nullptr;
-  auto dq_update = [&](int qt) {
+  auto dq_update = [&](int qt) __attribute__((always_inline)) {
     constexpr int NDB = C::DBLK / 2 > 0 ? C::DBLK / 2 : 1;
     const int qblk = wave & 1;
     f32x16 acc[NDB];
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   };
 
   const int kw = kv0 / 32;  // this wave's 32-key block index
-  auto step = [&](int t, auto buf_tag) {
+  auto step = [&](int t, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     using AHEAD = std::integral_constant<int, (BUF + 2) % 3>;
     const int qt = qt_of(t);
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
     const char* qbuf = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     const char* dbuf = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
     typename T::vec8 pf[2][2], sf[2][2];
-    auto scores = [&]() {
+    auto scores = [&]() __attribute__((always_inline)) {
       dkdv_scores<T, D, MOD>(qbuf, dbuf, BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2),
                           BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2), kf, vf, cx, qt * C::BM, my_key, masked,
                           rows_first, rows_count, BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2), has_doc, my_doc,
@@ -1317,12 +1317,13 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if ((stages & 2) && nkt > 0) {
-    // Paired waves at D = 128; at D = 64 a tile has half the matrix work
-    // against the same softmax work, so wave A's vector ALU sets the pace
-    // and the single-wave kernel measured faster.
+    // Paired waves at D = 128, and at D = 64 without block masks.  With a
+    // block mask at D = 64 the single-wave kernel measured faster: a tile has
+    // half the matrix work against the same softmax work, and the paired
+    // kernel reads the block lists with vector loads it must wait for.
     if (atomic_dq)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, true>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
-    else if constexpr (D == 128)
+    else if constexpr (D == 128 || !(MOD & 4))
       hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, MOD>), dim3(nkt * a.Hq * a.B), dim3(512), 0, s, a, partial);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);

@@ -198,7 +198,7 @@ attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype,
  *             atomics in either schedule; at D = 128 their kernels differ,
  *             so dK of 0 and 1 agree to rounding, not bitwise.
  *             On gfx950 fp32 device atomics sustain only a few hundred G
- *             adds/s, so 0 is the slower schedule here (about 4x on
+ *             adds/s, so 0 is the slower schedule here (about 1.4x on
  *             B1 H32/8 S2048 D128 causal); 1 is the fast path.
  *             Other values: INVALID_ARG.
  *   workspace : at least attn_bwd_workspace_size(p) bytes, 256-byte aligned
