@@ -49,6 +49,12 @@ CASES = [
     (1, 300, 300, 4, 2, 128, {"causal": True, "softcap": 5.0}),
     (1, 280, 280, 4, 4, 64, {"causal": True, "softcap": 2.0, "alibi": True}),
     (1, 160, 160, 2, 1, 128, {"causal": True, "scale": -0.09}),
+    (1, 256, 256, 2, 2, 128, {"window": (0, 0)}),        # each row sees only its own key
+    # a single key: dV is the plain sum of the rows' dO, so few rows keep it
+    # where bf16 output rounding (half a step) stays well below the bound
+    (1, 9, 1, 2, 1, 128, {}),
+    (1, 1, 700, 8, 1, 128, {}),                          # a single query
+    (1, 97, 97, 4, 2, 64, {"causal": True}),             # one ragged tile in each direction
 ]
 
 
@@ -285,3 +291,22 @@ def test_bwd_stages_equal_attn_bwd(b, case, deterministic):
     torch.cuda.synchronize()
     for x, y in zip((dq, dk, dv), ref):
         assert torch.equal(x, y)
+
+
+def test_bwd_empty_inputs(b):
+    """No keys: every row is empty (O = 0, LSE = -inf) and dQ is zero.  No
+    queries: no row reaches any key, so dK and dV are zero."""
+    q = torch.randn((1, 5, 4, 128), device="cuda").to(torch.bfloat16)
+    k0 = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = b.attn_fwd(q, k0, k0)
+    dq, dk, dv = b.attn_bwd(q, k0, k0, o, torch.randn_like(q), lse)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
+    q0 = torch.zeros((1, 0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.randn((1, 70, 2, 128), device="cuda").to(torch.bfloat16)
+    o0, lse0 = b.attn_fwd(q0, k, k, causal=True)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    _, dk, dv = b.attn_bwd(q0, k, k, o0, torch.zeros_like(q0), lse0, causal=True, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
