@@ -93,6 +93,8 @@ _lib.attn_bwd_stage.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_
                                 attn_tensor, attn_tensor, ctypes.c_void_p, attn_tensor,
                                 attn_tensor, attn_tensor, ctypes.c_int32, ctypes.c_void_p,
                                 ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+_lib.attn_fwd_workspace_size.restype = ctypes.c_size_t
+_lib.attn_fwd_workspace_size.argtypes = [_P(attn_params)]
 _lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
 _lib.attn_bwd_workspace_size.argtypes = [_P(attn_params)]
 _lib.attn_decode.restype = ctypes.c_int
@@ -124,6 +126,7 @@ _lib.block_mask_build.argtypes = [_P(attn_mask_desc), ctypes.c_int32, ctypes.c_i
                                   ctypes.c_void_p]
 
 EXPORTED = ["attn_status_string", "attn_last_error", "attn_fwd", "attn_fwd_tile_shape",
+            "attn_fwd_workspace_size",
             "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_size", "attn_decode",
             "attn_decode_kvcache", "attn_decode_workspace_size", "attn_block_mask_bytes",
             "block_mask_build"]
@@ -402,6 +405,11 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
 def decode_workspace_size(q, k_cache, num_splits=0, softcap=0.0, causal=False):
     p = _params(q, k_cache, q.shape[3], None, causal, (-1, -1), None, softcap, None)
     return _lib.attn_decode_workspace_size(ctypes.byref(p), int(num_splits))
+
+
+def fwd_workspace_size(q, k):
+    p = _params(q, k, q.shape[3], None, False, (-1, -1), None, 0.0, None)
+    return _lib.attn_fwd_workspace_size(ctypes.byref(p))
 
 
 def bwd_workspace_size(q, k):

@@ -330,6 +330,11 @@ attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k, a
                   1 << stage, stream);
 }
 
+size_t attn_fwd_workspace_size(const attn_params* p) {
+  (void)p;
+  return 0;
+}
+
 size_t attn_bwd_workspace_size(const attn_params* p) {
   if (p == nullptr || p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Sq < 0 || p->Sk < 0 || p->D <= 0)
     return 0;

@@ -173,6 +173,12 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k,
                      uint8_t* tile_trace, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Workspace bytes attn_fwd needs: 0 for every problem (the forward keeps
+ * its running softmax state on chip and writes only o and lse).  Declared so
+ * that callers size the workspaces of attn_fwd, attn_bwd and attn_decode the
+ * same way.  Host only; never fails. */
+size_t attn_fwd_workspace_size(const attn_params* p);
+
 /* Query / key tile sizes the forward uses for this problem (host only).
  * The tile trace has ceil(Sq/block_m) x ceil(Sk/block_n) entries per head. */
 attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype,

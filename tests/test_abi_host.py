@@ -116,6 +116,13 @@ def test_fwd_rejects_bad_tensors(b):
     assert st == 1 and "alibi" in err
 
 
+def test_fwd_workspace_size_is_zero(b):
+    lib = b.library()
+    for kw in ({}, {"causal": 1}, {"window": (64, 0)}, {"D": 128, "Sq": 4096, "Sk": 4096}):
+        assert lib.attn_fwd_workspace_size(ctypes.byref(params(b, **kw))) == 0
+    assert lib.attn_fwd_workspace_size(None) == 0
+
+
 def test_bwd_validation(b):
     lib = b.library()
     p = params(b)
