@@ -442,7 +442,7 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
   a.nhg = attn::decode_head_groups(p->Hq, p->Hkv, p->Sq);
   const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->Sq, p->D, a.parts);
   char* wsb = static_cast<char*>(workspace);
-  a.part_o = reinterpret_cast<float*>(wsb + wl.o_off);
+  a.part_o = reinterpret_cast<uint16_t*>(wsb + wl.o_off);
   a.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
   a.job_seg = reinterpret_cast<int32_t*>(wsb + wl.seg_off);
   return hip_status(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)), "attn_decode launch");

@@ -522,8 +522,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   // End of this wave's segment of job (cc.b, cc.jb), number `seg` of this
   // workgroup: the parity-1 wave of each head block hands its softmax state
   // to the parity-0 wave through its LDS slot (sequence flags, no barrier),
-  // and the parity-0 wave writes the merged partial result (normalised O in
-  // fp32, natural-log LSE) to slot w + j.  Waves whose head block has no
+  // and the parity-0 wave writes the merged partial result (normalised O,
+  // rounded to the input type: it is a convex combination of value rows, so
+  // it fits their range, and the combine reads half the bytes of fp32;
+  // natural-log LSE in fp32) to slot w + j.  Waves whose head block has no
   // query heads in this job still step the flags.
   auto finish_segment = [&](const Cursor& cc, bool job_end, int seg) {
     const bool active = hb * 32 < cc.rows;
@@ -556,15 +558,17 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       const int row = hb * 32 + c;
       const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
       const float s0 = a0 * inv, s1 = a1 * inv;
-      float* op = a.part_o + (slot * C::ROWS + row) * D;
+      uint16_t* op = a.part_o + (slot * C::ROWS + row) * D;
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float4 x = *reinterpret_cast<const float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4);
-          const float4 v4 = make_float4(oacc[db][4 * rr] * s0 + x.x * s1, oacc[db][4 * rr + 1] * s0 + x.y * s1,
-                                        oacc[db][4 * rr + 2] * s0 + x.z * s1, oacc[db][4 * rr + 3] * s0 + x.w * s1);
-          if (row < cc.rows) *reinterpret_cast<float4*>(op + 32 * db + 8 * rr + 4 * g) = v4;
+          const float o0 = oacc[db][4 * rr] * s0 + x.x * s1, o1 = oacc[db][4 * rr + 1] * s0 + x.y * s1;
+          const float o2 = oacc[db][4 * rr + 2] * s0 + x.z * s1, o3 = oacc[db][4 * rr + 3] * s0 + x.w * s1;
+          const uint2 w2 = make_uint2(f32_to_elem<T>(o0) | (uint32_t)f32_to_elem<T>(o1) << 16,
+                                      f32_to_elem<T>(o2) | (uint32_t)f32_to_elem<T>(o3) << 16);
+          if (row < cc.rows) *reinterpret_cast<uint2*>(op + 32 * db + 8 * rr + 4 * g) = w2;
         }
       if (g == 0 && row < cc.rows)
         a.part_lse[slot * C::ROWS + row] = l_tot > 0.0f ? (M + fast_log2(l_tot)) * kLn2 : kNegInf;
@@ -699,7 +703,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (Lb > 0) {
     const int w0 = a.job_seg[2 * j], w1 = a.job_seg[2 * j + 1];
     const float* pl = a.part_lse + ((int64_t)w0 + j) * ROWS + r;
-    const float* po = a.part_o + (((int64_t)w0 + j) * ROWS + r) * D + 4 * d4;
+    const uint16_t* po = a.part_o + (((int64_t)w0 + j) * ROWS + r) * D + 4 * d4;
     const int ns = w1 - w0 + 1;
     for (int s0 = 0; s0 < ns; s0 += U) {
       float ls[U];
@@ -708,8 +712,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       for (int e = 0; e < U; ++e) {
         const bool ok = s0 + e < ns;
         ls[e] = ok ? pl[(int64_t)(s0 + e) * ROWS] : kNegInf;
-        ov[e] = ok ? *reinterpret_cast<const float4*>(po + (int64_t)(s0 + e) * ROWS * D)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint2 w2 = ok ? *reinterpret_cast<const uint2*>(po + (int64_t)(s0 + e) * ROWS * D) : make_uint2(0, 0);
+        ov[e] = make_float4(T::to_f32(w2.x & 0xffffu), T::to_f32(w2.x >> 16), T::to_f32(w2.y & 0xffffu),
+                            T::to_f32(w2.y >> 16));
       }
       float mr = m;
 #pragma unroll
@@ -828,7 +833,7 @@ DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int part
   const size_t jobs = (size_t)B * Hkv * decode_head_groups(Hq, Hkv, Sq);
   const size_t slots = (size_t)parts + jobs;
   w.o_off = 0;
-  w.lse_off = (slots * kDecodeRows * D * sizeof(float) + 255) / 256 * 256;
+  w.lse_off = (slots * kDecodeRows * D * sizeof(uint16_t) + 255) / 256 * 256;
   w.seg_off = w.lse_off + (slots * kDecodeRows * sizeof(float) + 255) / 256 * 256;
   w.bytes = w.seg_off + (jobs * 2 * sizeof(int32_t) + 255) / 256 * 256;
   return w;

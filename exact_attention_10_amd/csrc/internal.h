@@ -116,7 +116,8 @@ struct DecodeArgs {
   float softcap;
   int parts;                 // workgroups; the key work is cut into this many equal ranges
   int nhg;                   // groups of up to kDecodeRows query heads per kv head
-  float* part_o;             // workspace [parts + jobs][kDecodeRows][D]
+  uint16_t* part_o;          // workspace [parts + jobs][kDecodeRows][D]: normalised partial O,
+                             // rounded to the input type
   float* part_lse;           // workspace [parts + jobs][kDecodeRows]
                              // (a job: sequence, kv head, up to kDecodeRows rows)
   int32_t* job_seg;          // workspace [jobs][2]: first and last workgroup of each job
