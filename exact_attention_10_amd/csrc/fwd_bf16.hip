@@ -240,6 +240,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
   __shared__ __attribute__((aligned(16))) char lds_v1_[NG * C::TB];
   __shared__ int lds_doc0_[NG * C::BN];
   __shared__ int lds_doc1_[NG * C::BN];
+  __shared__ int lds_gsync_[NG];  // arrivals of each group's waves at its step barriers
 
   const int tid_wg = threadIdx.x;
   const int wave_wg = __builtin_amdgcn_readfirstlane(tid_wg >> 6);
@@ -392,8 +393,32 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     load_tile(tile_at(grp).kt, B0{});
     store_doc(B0{});
   }
+  if (tid_wg < NG) lds_gsync_[tid_wg] = 0;
   wait_dma();
   __syncthreads();
+
+  // With two groups, each group ends its steps with a barrier of its own
+  // four waves (an arrival count in LDS, bounded spin), so the groups do not
+  // run in lockstep and one group's softmax can overlap the other's matrix
+  // work on the same SIMD.  The tile buffers are per group, so a group
+  // barrier orders everything a step needs: copies landed before reads, and
+  // reads of a buffer done before the next copy into it.
+  int nsync = 0;
+  auto step_sync = [&]() __attribute__((always_inline)) {
+    if constexpr (NG == 1) {
+      __syncthreads();
+    } else {
+      ++nsync;
+      if (lane == 0) __hip_atomic_fetch_add(&lds_gsync_[grp], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      const int target = C::WPG * nsync;
+      for (int n = 0; n < (1 << 22); ++n) {
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&lds_gsync_[grp], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (v >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  };
 
   // Per-row allowed key interval [lo, lo + span) for partial tiles; an empty
   // row (or a row past Sq) has span 0.
@@ -427,7 +452,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     }
     if (has_next) store_doc(NEXT{});
     wait_dma();
-    __syncthreads();
+    step_sync();
   };
   using FULL = std::false_type;
   using PART = std::true_type;
@@ -449,8 +474,10 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
 
   if constexpr (NG == 2) {
     // Group 1 hands its running state (max, partial sums, unnormalised O)
-    // to group 0 through LDS (the tile buffers are free after the last
-    // step's barrier); wave w of each group owns the same 32 rows.
+    // to group 0 through LDS; wave w of each group owns the same 32 rows.
+    // The slots overlap group 0's tile buffers, and the step barriers are per
+    // group, so first both groups must be past their last step.
+    __syncthreads();
     constexpr int SLOT = 64 * (16 * C::DBLK + 2);  // floats per wave
     static_assert(SLOT * 4 <= C::TB, "state slot fits one tile buffer");
     float* st = reinterpret_cast<float*>((wave < 2 ? lds_k0_ : lds_k1_) + (wave & 1) * C::TB);
@@ -464,7 +491,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
       st[16 * C::DBLK * 64 + lane] = m_run;
       st[16 * C::DBLK * 64 + 64 + lane] = l_run;
     }
-    __syncthreads();
+    __syncthreads();  // group 1's state is in LDS
     if (grp == 1) return;
     const float mo = st[16 * C::DBLK * 64 + lane];
     const float lo = st[16 * C::DBLK * 64 + 64 + lane];

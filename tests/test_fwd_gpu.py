@@ -69,6 +69,10 @@ CASES = [
     (1, 280, 280, 4, 4, 64, {"causal": True, "softcap": 2.0, "alibi": True}),
     (1, 65, 1, 2, 1, 128, {}),                           # a single key
     (1, 1, 700, 8, 1, 128, {}),                          # a single query
+    # three 64-key tiles for every query tile: of the two key-tile groups of a
+    # small-grid workgroup, group 1 ends a tile before group 0 (its state
+    # hand-over must wait for group 0's last tile)
+    (1, 384, 130, 8, 2, 128, {}),
 ]
 
 
