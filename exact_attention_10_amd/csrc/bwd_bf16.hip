@@ -1125,7 +1125,7 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
 }
 
 template <typename T, int D, int MOD>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int fold) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(16))) char lk0[C::TB];
   __shared__ __attribute__((aligned(16))) char lk1[C::TB];
@@ -1139,7 +1139,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int g = lane >> 5, c = lane & 31;
   const int nqt = (a.Sq + C::BM - 1) / C::BM;
   const int per = a.Hq * a.B;
-  const int qt = nqt - 1 - blockIdx.x / per;
+  // Query tiles heaviest first; with fold > 0 the grid rows from fold on run
+  // lightest first instead.  Two workgroups share a CU, and when the whole
+  // grid is resident at once the dispatcher pairs workgroup x with x + (the
+  // number of CUs), so folding pairs heavy causal tiles with light ones.
+  const int u_row = blockIdx.x / per;
+  const int qt = (fold == 0 || u_row < fold) ? nqt - 1 - u_row : u_row - fold;
   const int rem = blockIdx.x % per;
   const int b = rem / a.Hq;
   int h = rem % a.Hq;
@@ -1312,7 +1317,12 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   // Delta and lse2 for the dK/dV kernel (no separate Delta pass).
   const int nqt0 = (a.Sq + QCfg<D>::BM - 1) / QCfg<D>::BM;
   if ((stages & 1) && !atomic_dq && nqt0 > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MOD>), dim3(nqt0 * a.Hq * a.B), dim3(256), 0, s, a);
+    // Fold the tile order (see the kernel) when causal work is uneven and the
+    // grid fits the GPU at two workgroups per CU; a larger grid is balanced
+    // by dispatching heaviest first as CUs free up.
+    const long grid = (long)nqt0 * a.Hq * a.B;
+    const int fold = (a.mask.causal && !(MOD & 4) && grid <= 2L * device_cu_count()) ? (nqt0 + 1) / 2 : 0;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MOD>), dim3(nqt0 * a.Hq * a.B), dim3(256), 0, s, a, fold);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

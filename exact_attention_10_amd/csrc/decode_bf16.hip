@@ -814,8 +814,7 @@ int decode_head_groups(int Hq, int Hkv, int Sq) {
   return (int)(((int64_t)Sq * (Hq / Hkv) + kDecodeRows - 1) / kDecodeRows);
 }
 
-int decode_parts(int num_splits) {
-  if (num_splits > 0) return num_splits;
+int device_cu_count() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -827,6 +826,8 @@ int decode_parts(int num_splits) {
   }
   return cus[dev];
 }
+
+int decode_parts(int num_splits) { return num_splits > 0 ? num_splits : device_cu_count(); }
 
 DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int parts) {
   DecodeWorkspace w;

@@ -138,6 +138,7 @@ struct DecodeArgs {
 constexpr int kDecodeRows = 128;  // rows (query, head) per decode job
 // Number of workgroups: num_splits when > 0, else the device's compute units.
 int decode_parts(int num_splits);
+int device_cu_count();  // compute units of the current device (cached per device)
 int decode_head_groups(int Hq, int Hkv, int Sq);  // jobs per (sequence, kv head)
 struct DecodeWorkspace {
   size_t o_off, lse_off, seg_off, bytes;
