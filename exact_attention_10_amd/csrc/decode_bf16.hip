@@ -15,11 +15,12 @@
 // Work decomposition.  A job is one (sequence b, kv head, group of up to 128
 // rows of that kv head), a row being a (query t, query head) pair numbered
 // t * G + head (G query heads per kv head); its keys are cut into 32-key
-// steps.  All
-// jobs' steps, in job order, form one list of S steps that is cut into
-// Pe = min(P, S) equal contiguous ranges, one per workgroup (P = one per
-// compute unit by default), so every workgroup streams the same number of K/V
-// bytes whatever the mix of cache lengths.  A range that spans several jobs
+// steps.  All jobs, in job order, form one list of S units -- each job SEG
+// units of segment weight (its query load, state merge and partial write)
+// followed by its steps -- that is cut into Pe = min(P, S) equal contiguous
+// ranges, one per workgroup (P = one per compute unit by default), so every
+// workgroup gets the same work whatever the mix of cache lengths, a
+// workgroup that starts a job taking fewer key steps.  A range that spans several jobs
 // produces one partial result per job; the partial of job j from workgroup w
 // goes to slot w + j (unique, since ranges are ordered).  The workgroups that
 // start and end a job record their index for the combine kernel.
@@ -62,6 +63,10 @@ struct DecCfg {
   static constexpr int DEPTH = NS - 1;                // items a producer keeps unpublished in flight
   static constexpr int PER = 2 * GROUPS / NWP;        // copies per producer lane per ring item
   static constexpr int WIN = 512;                     // cache lengths kept in LDS
+  // Schedule weight of a job segment (query load, state merge, partial
+  // write) in 32-key steps: each job counts SEG extra units in the split, so
+  // a workgroup that starts a job takes that many fewer key steps.
+  static constexpr int SEG = 4;
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
   static constexpr int MSLOT = 64 * (16 * DBLK + 2);  // floats of one wave's softmax state
@@ -207,12 +212,13 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   if (a.B <= C::NT) {  // one pass: every thread keeps its sequence's length
     const int Lt = tid < a.B ? seq_len(a, tid) : 0;
     const int n = (Lt + C::BN - 1) / C::BN;
-    const long long pre = block_excl_scan<C::NWT>((long long)n * jpb, red, &S);
+    const long long units = n > 0 ? (long long)(n + C::SEG) * jpb : 0;
+    const long long pre = block_excl_scan<C::NWT>(units, red, &S);
     const int Pe = S < P ? (int)S : P;
     if (w_id >= Pe) return;
     lo = (long long)w_id * S / Pe;
     hi = (long long)(w_id + 1) * S / Pe;
-    if (n > 0 && pre <= lo && lo < pre + (long long)n * jpb) {
+    if (n > 0 && pre <= lo && lo < pre + units) {
       sh_b0 = tid;
       sh_off0 = lo - pre;
     }
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     for (int base = 0; base < a.B; base += C::NT) {
       const int b = base + tid;
       const int n = b < a.B ? (seq_len(a, b) + C::BN - 1) / C::BN : 0;
-      S += block_sum<C::NWT>(n, red);
+      S += block_sum<C::NWT>(n > 0 ? n + C::SEG : 0, red);
     }
     S *= jpb;
     const int Pe = S < P ? (int)S : P;
@@ -236,9 +242,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     for (int base = 0; base < a.B; base += C::NT) {
       const int b = base + tid;
       const int n = b < a.B ? (seq_len(a, b) + C::BN - 1) / C::BN : 0;
+      const long long units = n > 0 ? (long long)(n + C::SEG) * jpb : 0;
       long long tot;
-      const long long pre = carry + block_excl_scan<C::NWT>((long long)n * jpb, red, &tot);
-      if (n > 0 && pre <= lo && lo < pre + (long long)n * jpb) {
+      const long long pre = carry + block_excl_scan<C::NWT>(units, red, &tot);
+      if (n > 0 && pre <= lo && lo < pre + units) {
         sh_b0 = b;
         sh_off0 = lo - pre;
       }
@@ -283,11 +290,16 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     cu.b = b0;
     cu.Lb = len_of(b0);
     cu.n = (cu.Lb + C::BN - 1) / C::BN;
+    // The range starts in job jb at unit pos; a job's first SEG units are
+    // its segment weight, so a start inside them means the job's first step
+    // (and the rest of those units come out of the range).
     const int off = (int)sh_off0;
-    cu.jb = off / cu.n;
-    cu.step = off - cu.jb * cu.n;
+    const int per_job = cu.n + C::SEG;
+    cu.jb = off / per_job;
+    const int pos = off - cu.jb * per_job;
+    cu.step = pos < C::SEG ? 0 : pos - C::SEG;
     cu.phase = 0;
-    cu.left = (int)(hi - lo);
+    cu.left = (int)(hi - lo) - (pos < C::SEG ? C::SEG - pos : 0);  // <= 0: no key step here
     set_job(cu);
   };
   auto advance = [&](Cursor& cu) {
@@ -298,6 +310,13 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     --cu.left;
     ++cu.step;
     if (cu.left == 0 || cu.step < cu.n) return;
+    // the next job's segment weight comes first; a range that ends inside
+    // it has no key step of that job
+    if (cu.left <= C::SEG) {
+      cu.left = 0;
+      return;
+    }
+    cu.left -= C::SEG;
     cu.step = 0;
     cu.phase = 0;
     if (++cu.jb == jpb) {

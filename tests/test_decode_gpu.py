@@ -50,11 +50,15 @@ def test_decode_mqa_full(b):
     dict(B=2, Hq=40, Hkv=8, D=64, Smax=1000, lens=[999, 1000], softcap=3.0),
     dict(B=600, Hq=8, Hkv=8, D=64, Smax=40, lens="random"),
     dict(B=3, Hq=320, Hkv=1, D=128, Smax=100, lens=[100, 1, 33]),
+    # more sequences than threads in a workgroup: the schedule scan runs in
+    # several passes, and lengths past the LDS window are read from memory
+    dict(B=700, Hq=8, Hkv=8, D=64, Smax=24, lens="random"),
 ])
 def test_decode_ragged(b, cfg):
     """Ragged cache lengths (1, tile edges, empty caches), GQA groups that
     do not fill a 128-head job or span several, softcap, one workgroup over
-    hundreds of sequences, more workgroups than key steps."""
+    hundreds of sequences, more workgroups than key steps, more sequences than
+    a workgroup has threads."""
     w = inputs.decode_mqa(seed=11, B=cfg["B"], Hq=cfg["Hq"], Smax=cfg["Smax"], D=cfg["D"],
                           lmin=1, lmax=cfg["Smax"])
     if cfg["Hkv"] > 1:
