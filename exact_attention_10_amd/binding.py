@@ -125,7 +125,11 @@ _lib.block_mask_build.argtypes = [_P(attn_mask_desc), ctypes.c_int32, ctypes.c_i
                                   ctypes.c_void_p, ctypes.c_size_t, _P(attn_block_mask),
                                   ctypes.c_void_p]
 
-EXPORTED = ["attn_status_string", "attn_last_error", "attn_fwd", "attn_fwd_tile_shape",
+_lib.attn_debug_set_spin_limit.restype = None
+_lib.attn_debug_set_spin_limit.argtypes = [ctypes.c_int32]
+
+EXPORTED = ["attn_status_string", "attn_last_error", "attn_debug_set_spin_limit",
+            "attn_fwd", "attn_fwd_tile_shape",
             "attn_fwd_workspace_size",
             "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_size", "attn_decode",
             "attn_decode_kvcache", "attn_decode_workspace_size", "attn_block_mask_bytes",
@@ -206,13 +210,24 @@ class BlockMask:
 def block_mask_build(B, Sq, Sk, block_m=128, block_n=128, causal=False, window=(-1, -1),
                      doc_q=None, doc_k=None, device="cuda"):
     """Build a block mask on the device (doc_q / doc_k: int32 [B, S] device tensors)."""
+    if (doc_q is None) != (doc_k is None):
+        raise ValueError("give both doc_q and doc_k or neither")
+    if doc_q is not None:
+        _need_shape("doc_q", doc_q, (B, Sq))
+        _need_shape("doc_k", doc_k, (B, Sk))
+        _need_dtype("doc_q", doc_q, torch.int32)
+        _need_dtype("doc_k", doc_k, torch.int32)
+        if doc_q.device.type != "cuda" or doc_k.device != doc_q.device:
+            raise ValueError("doc_q and doc_k must be on one GPU")
+        if torch.device(device) != doc_q.device and torch.device(device).index is not None:
+            raise ValueError("doc_q is on %s, the mask is built on %s" % (doc_q.device, device))
+        device = doc_q.device
     desc = attn_mask_desc()
     desc.causal = int(bool(causal))
     desc.window_left, desc.window_right = int(window[0]), int(window[1])
     if doc_q is not None:
         doc_q = doc_q.contiguous()
         doc_k = doc_k.contiguous()
-        assert doc_q.dtype == torch.int32 and doc_k.dtype == torch.int32
     desc.doc_q = None if doc_q is None else doc_q.data_ptr()
     desc.doc_k = None if doc_k is None else doc_k.data_ptr()
     nbytes = _lib.attn_block_mask_bytes(B, Sq, Sk, block_m, block_n)
@@ -224,6 +239,74 @@ def block_mask_build(B, Sq, Sk, block_m=128, block_n=128, causal=False, window=(
     return BlockMask(out, buf, doc_q, doc_k)
 
 
+def _shape_of(t):
+    return tuple(int(x) for x in t.shape)
+
+
+def _need_shape(name, t, shape):
+    if _shape_of(t) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), _shape_of(t)))
+
+
+def _need_dtype(name, t, dtype):
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _need_contig(name, t):
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _need_device(q, **tensors):
+    """Every tensor the library reads or writes lives on q's GPU: the C ABI
+    takes raw device pointers, so a host tensor or one on another device
+    would reach a kernel as an invalid address."""
+    if q.device.type != "cuda":
+        raise ValueError("q must be a GPU tensor (got device %s)" % q.device)
+    for name, t in tensors.items():
+        if t is not None and t.device != q.device:
+            raise ValueError("%s is on %s, q on %s: every tensor must be on q's device"
+                             % (name, t.device, q.device))
+
+
+def _check_qkv(q, k, v):
+    """q [B, Sq, Hq, D], k and v [B, Sk, Hkv, D] of one dtype."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError("%s must be a 4-d [B, S, H, D] tensor, got shape %s"
+                             % (name, _shape_of(t)))
+    B, _, _, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("k must be [B=%d, Sk, Hkv, D=%d], got %s" % (B, D, _shape_of(k)))
+    _need_shape("v", v, k.shape)
+    _need_dtype("k", k, q.dtype)
+    _need_dtype("v", v, q.dtype)
+
+
+def _check_like(name, t, ref):
+    if t is not None:
+        _need_shape(name, t, ref.shape)
+        _need_dtype(name, t, ref.dtype)
+
+
+def _check_lse(lse, B, Hq, Sq):
+    if lse is not None:
+        _need_shape("lse", lse, (B, Hq, Sq))
+        _need_dtype("lse", lse, torch.float32)
+        _need_contig("lse", lse)
+
+
+def _check_alibi(alibi_slopes, B, Hq):
+    if alibi_slopes is None:
+        return
+    _need_dtype("alibi_slopes", alibi_slopes, torch.float32)
+    _need_contig("alibi_slopes", alibi_slopes)
+    if _shape_of(alibi_slopes) not in ((Hq,), (B, Hq)):
+        raise ValueError("alibi_slopes must be (Hq,) = (%d,) or (B, Hq) = (%d, %d), got %s"
+                         % (Hq, B, Hq, _shape_of(alibi_slopes)))
+
+
 def _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask):
     p = attn_params()
     p.B, p.Sq, p.Hq = q.shape[0], q.shape[1], q.shape[2]
@@ -233,8 +316,7 @@ def _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block
     p.causal = int(bool(causal))
     p.window_left, p.window_right = int(window[0]), int(window[1])
     if alibi_slopes is not None:
-        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous():
-            raise ValueError("alibi_slopes must be a contiguous float32 tensor")
+        _check_alibi(alibi_slopes, p.B, p.Hq)
         p.alibi_slopes = alibi_slopes.data_ptr()
         p.alibi_batch_stride = 0 if alibi_slopes.dim() == 1 else alibi_slopes.shape[-1]
     else:
@@ -258,7 +340,22 @@ def tile_shape(q, k, block_mask=None, causal=False):
 def attn_fwd(q, k, v, softmax_scale=None, causal=False, window=(-1, -1), alibi_slopes=None,
              softcap=0.0, block_mask=None, out=None, lse=None, tile_trace=None):
     """Forward attention.  Returns (out [B, Sq, Hq, D], lse fp32 [B, Hq, Sq])."""
+    _check_qkv(q, k, v)
     B, Sq, Hq, D = q.shape
+    _check_like("out", out, q)
+    _check_lse(lse, B, Hq, Sq)
+    _check_alibi(alibi_slopes, B, Hq)
+    if tile_trace is not None:
+        _need_dtype("tile_trace", tile_trace, torch.uint8)
+        _need_contig("tile_trace", tile_trace)
+        bm, bn = tile_shape(q, k, block_mask, causal)
+        n = B * Hq * (-(-Sq // bm)) * (-(-k.shape[1] // bn))
+        if tile_trace.numel() != n:
+            raise ValueError("tile_trace must hold B*Hq*nQt*nKt = %d entries, got %d"
+                             % (n, tile_trace.numel()))
+    _need_device(q, k=k, v=v, out=out, lse=lse, tile_trace=tile_trace,
+                 alibi_slopes=alibi_slopes,
+                 block_mask=None if block_mask is None else block_mask.buffer)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -273,7 +370,22 @@ def attn_bwd(q, k, v, out, dout, lse, softmax_scale=None, causal=False, window=(
              alibi_slopes=None, softcap=0.0, deterministic=True, dq=None, dk=None, dv=None,
              workspace=None, block_mask=None):
     """Backward attention from the saved LSE.  Returns (dq, dk, dv)."""
-    D = q.shape[3]
+    _check_qkv(q, k, v)
+    B, Sq, Hq, D = q.shape
+    _check_like("out", out, q)
+    _check_like("dout", dout, q)
+    if lse is None:
+        raise ValueError("lse (the forward's log-sum-exp) is required")
+    _check_lse(lse, B, Hq, Sq)
+    _check_alibi(alibi_slopes, B, Hq)
+    _check_like("dq", dq, q)
+    _check_like("dk", dk, k)
+    _check_like("dv", dv, v)
+    if workspace is not None:
+        _need_dtype("workspace", workspace, torch.uint8)
+    _need_device(q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv,
+                 workspace=workspace, alibi_slopes=alibi_slopes,
+                 block_mask=None if block_mask is None else block_mask.buffer)
     p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -340,7 +452,16 @@ def attn_bwd_stage(stage, q, k, v, out, dout, lse, dq, dk, dv, workspace, softma
     """Enqueue one stage of attn_bwd (deterministic: 0 dQ with Delta, 1 dK/dV,
     2 group sum, 3 nothing; see attn.h); stages 0..3 in order with one
     workspace equal attn_bwd."""
-    D = q.shape[3]
+    _check_qkv(q, k, v)
+    B, Sq, Hq, D = q.shape
+    for name, t, ref in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k),
+                         ("dv", dv, v)):
+        _check_like(name, t, ref)
+    _check_lse(lse, B, Hq, Sq)
+    _need_dtype("workspace", workspace, torch.uint8)
+    _need_device(q, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv,
+                 workspace=workspace, alibi_slopes=alibi_slopes,
+                 block_mask=None if block_mask is None else block_mask.buffer)
     p = _params(q, k, D, softmax_scale, causal, window, alibi_slopes, softcap, block_mask)
     _check(_lib.attn_bwd_stage(ctypes.byref(p), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
                                _tensor(dout), _ptr(lse), _tensor(dq), _tensor(dk), _tensor(dv),
@@ -358,24 +479,55 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
     cache_batch_idx int32 [B] (contiguous caches) and k_new / v_new
     [B, s_new, Hkv, D] appended in place at rows [L_b, L_b + s_new).
     Returns (out, lse [B, Hq, Sq])."""
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q and the caches must be 4-d tensors")
     B, Sq, Hq, D = q.shape
+    if k_cache.shape[3] != D:
+        raise ValueError("k_cache head dim %d differs from q's %d" % (k_cache.shape[3], D))
+    _check_like("v_cache", v_cache, k_cache)
+    _need_dtype("k_cache", k_cache, q.dtype)
+    Hkv = k_cache.shape[2]
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2:
+            raise ValueError("block_table must be a 2-d int32 tensor")
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must have B = %d rows, got %d" % (B, block_table.shape[0]))
+        _need_contig("block_table", block_table)
+    elif cache_batch_idx is None and k_cache.shape[0] != B:
+        raise ValueError("k_cache must have B = %d batch rows, got %d" % (B, k_cache.shape[0]))
+    if cache_batch_idx is not None:
+        _need_shape("cache_batch_idx", cache_batch_idx, (B,))
+        _need_dtype("cache_batch_idx", cache_batch_idx, torch.int32)
+        _need_contig("cache_batch_idx", cache_batch_idx)
+    _need_shape("cache_seqlens", cache_seqlens, (B,))
+    _need_dtype("cache_seqlens", cache_seqlens, torch.int32)
+    _need_contig("cache_seqlens", cache_seqlens)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must be given together")
+    if k_new is not None:
+        if k_new.dim() != 4 or k_new.shape[0] != B or tuple(k_new.shape[2:]) != (Hkv, D):
+            raise ValueError("k_new must be [B=%d, s_new, Hkv=%d, D=%d], got %s"
+                             % (B, Hkv, D, _shape_of(k_new)))
+        _check_like("v_new", v_new, k_new)
+        _need_dtype("k_new", k_new, q.dtype)
+    _check_like("out", out, q)
+    _check_lse(lse, B, Hq, Sq)
+    if workspace is not None:
+        _need_dtype("workspace", workspace, torch.uint8)
+    _need_device(q, k_cache=k_cache, v_cache=v_cache, cache_seqlens=cache_seqlens,
+                 block_table=block_table, cache_batch_idx=cache_batch_idx, k_new=k_new,
+                 v_new=v_new, out=out, lse=lse, workspace=workspace)
     p = _params(q, k_cache, D, softmax_scale, causal, (-1, -1), None, softcap, None)
     kv = None
     if block_table is not None or cache_batch_idx is not None or k_new is not None:
         kv = attn_kvcache()
         if block_table is not None:
-            if block_table.dtype != torch.int32 or block_table.dim() != 2:
-                raise ValueError("block_table must be a 2-d int32 tensor")
-            if not block_table.is_contiguous():
-                raise ValueError("block_table must be contiguous")
             kv.block_table = block_table.data_ptr()
             kv.max_blocks = block_table.shape[1]
             kv.page_size = k_cache.shape[1]
             kv.num_pages = k_cache.shape[0]
             p.Sk = block_table.shape[1] * k_cache.shape[1]
         if cache_batch_idx is not None:
-            if cache_batch_idx.dtype != torch.int32:
-                raise ValueError("cache_batch_idx must be int32")
             kv.cache_batch_idx = cache_batch_idx.data_ptr()
             kv.cache_batch = k_cache.shape[0]
         if k_new is not None:
@@ -385,11 +537,10 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    if cache_seqlens.dtype != torch.int32:
-        raise ValueError("cache_seqlens must be int32")
     need = _lib.attn_decode_workspace_size(ctypes.byref(p), int(num_splits))
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        # zeroed: its first word is the sticky status word (decode_status)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device)
     if kv is None:
         _check(_lib.attn_decode(ctypes.byref(p), _tensor(q), _tensor(k_cache), _tensor(v_cache),
                                 _ptr(cache_seqlens), int(num_splits), _tensor(out), _ptr(lse),
@@ -400,6 +551,19 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
                                         int(num_splits), _tensor(out), _ptr(lse), _ptr(workspace),
                                         workspace.numel(), _stream()))
     return out, lse
+
+
+def decode_status(workspace):
+    """The sticky status word at the start of a decode workspace (reads the
+    device; call after the decode): bit 1 = a cache length was out of range
+    and clamped, bit 2 = an in-kernel wait reached its bound."""
+    return int(workspace[:4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
+def set_spin_limit(limit):
+    """Testing hook (attn_debug_set_spin_limit): bound of the in-kernel
+    waits for later launches; a negative value restores the default."""
+    _lib.attn_debug_set_spin_limit(int(limit))
 
 
 def decode_workspace_size(q, k_cache, num_splits=0, softcap=0.0, causal=False):

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -10,6 +11,13 @@
 
 #include "attn.h"
 #include "internal.h"
+
+namespace attn {
+namespace {
+std::atomic<int> g_spin_limit{kDefaultSpinLimit};
+}
+int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+}  // namespace attn
 
 namespace {
 
@@ -89,6 +97,13 @@ void strides3(const attn_tensor& t, int64_t* sb, int64_t* ss, int64_t* sh) {
   *sh = t.stride[2];
 }
 
+// A window side of Sq + Sk or more excludes no key (every |i + delta - j|
+// is smaller), so it is the unbounded side; mapping it to -1 keeps the
+// kernels' index arithmetic (sums of positions and window sides) inside int.
+int32_t window_side(int32_t side, int32_t Sq, int32_t Sk) {
+  return side >= 0 && (int64_t)side >= (int64_t)Sq + Sk ? -1 : side;
+}
+
 attn::MaskArgs mask_from(const attn_params* p) {
   attn::MaskArgs m{};
   if (p->block_mask != nullptr) {
@@ -103,6 +118,8 @@ attn::MaskArgs mask_from(const attn_params* p) {
     m.wr = p->window_right;
     m.doc_q = m.doc_k = nullptr;
   }
+  m.wl = window_side(m.wl, p->Sq, p->Sk);
+  m.wr = window_side(m.wr, p->Sq, p->Sk);
   return m;
 }
 
@@ -149,6 +166,10 @@ const char* attn_status_string(attn_status s) {
 }
 
 const char* attn_last_error(void) { return g_err; }
+
+void attn_debug_set_spin_limit(int32_t limit) {
+  attn::g_spin_limit.store(limit < 0 ? attn::kDefaultSpinLimit : limit, std::memory_order_relaxed);
+}
 
 attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype, int32_t* block_m,
                                 int32_t* block_n) {
@@ -203,6 +224,7 @@ attn_status attn_fwd(const attn_params* p, attn_tensor q, attn_tensor k, attn_te
   a.alibi_sb = p->alibi_batch_stride;
   a.softcap = p->softcap;
   a.mask = mask_from(p);
+  a.spin_limit = attn::spin_limit();
   if (p->block_mask != nullptr) {
     const attn_block_mask* bm = p->block_mask;
     a.tiles.kv_num_full = bm->kv_num_full;
@@ -442,6 +464,8 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
   a.nhg = attn::decode_head_groups(p->Hq, p->Hkv, p->Sq);
   const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->Sq, p->D, a.parts);
   char* wsb = static_cast<char*>(workspace);
+  a.status = reinterpret_cast<uint32_t*>(wsb + wl.status_off);
+  a.spin_limit = attn::spin_limit();
   a.part_o = reinterpret_cast<uint16_t*>(wsb + wl.o_off);
   a.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
   a.job_seg = reinterpret_cast<int32_t*>(wsb + wl.seg_off);
@@ -511,8 +535,8 @@ attn_status block_mask_build(const attn_mask_desc* m, int32_t B, int32_t Sq, int
   attn::BlockMaskArgs a{};
   a.B = B; a.Sq = Sq; a.Sk = Sk; a.bm = block_m; a.bn = block_n; a.nQ = nQ; a.nK = nK;
   a.mask.causal = m->causal;
-  a.mask.wl = m->window_left;
-  a.mask.wr = m->window_right;
+  a.mask.wl = window_side(m->window_left, Sq, Sk);
+  a.mask.wr = window_side(m->window_right, Sq, Sk);
   a.mask.doc_q = m->doc_q;
   a.mask.doc_k = m->doc_k;
   a.cls = r.cls;

@@ -73,12 +73,17 @@ struct DecCfg {
 };
 
 // Bounded spin on an LDS flag: the waves of a workgroup hand items over with
-// counters instead of barriers.  The bound (about 2^22 sleeps) only matters if
-// the protocol were broken; it keeps every wave finite.
-constexpr int kSpinLimit = 1 << 22;
+// counters instead of barriers.  The bound (spin_limit sleeps, about 2^22 by
+// default) only matters if the protocol were broken; it keeps every wave
+// finite.  Returns false when the bound was reached with the condition still
+// false: the caller then marks its results as poisoned.
 template <typename Pred>
-__device__ __forceinline__ void spin_until(Pred pred) {
-  for (int n = 0; !pred() && n < kSpinLimit; ++n) __builtin_amdgcn_s_sleep(1);
+__device__ __forceinline__ bool spin_until(Pred pred, int limit) {
+  for (int n = 0; n < limit; ++n) {
+    if (pred()) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return pred();
 }
 __device__ __forceinline__ int lds_acquire(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -86,8 +91,12 @@ __device__ __forceinline__ int lds_acquire(const int* p) {
 __device__ __forceinline__ void publish(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void spin_until_ge(const int* p, int v) {
-  spin_until([&] { return lds_acquire(p) >= v; });
+__device__ __forceinline__ bool spin_until_ge(const int* p, int v, int limit) {
+  return spin_until([&] { return lds_acquire(p) >= v; }, limit);
+}
+// Set bits of the sticky status word (a device-scope vector atomic).
+__device__ __forceinline__ void status_or(uint32_t* status, uint32_t bits) {
+  __hip_atomic_fetch_or(status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int clamp_len(int L, int smax) { return L < 0 ? 0 : (L > smax ? smax : L); }
@@ -194,6 +203,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   __shared__ int landed[C::NWP];       // items whose copies by producer p have landed
   __shared__ int consumed[C::NWC];     // items consumer wave w is done with
   __shared__ int mrg_written[4], mrg_read[4];  // merge handshakes per head block
+  __shared__ int ring_broken;          // some wave's wait expired (its data may be stale)
   __shared__ long long sh_b0, sh_off0;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -259,8 +269,18 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   if (tid < C::NWP) landed[tid] = 0;
   if (tid < C::NWC) consumed[tid] = 0;
   if (tid < 4) mrg_written[tid] = mrg_read[tid] = 0;
+  if (tid == 0) ring_broken = 0;
   __syncthreads();
   const int b0 = (int)sh_b0;
+  // A wait of this wave that expired: its data may be stale, so the rows it
+  // contributes to are written as NaN and the status word records it.
+  bool broken = false;
+  auto note = [&](bool ok) {
+    if (!ok) {
+      broken = true;
+      ring_broken = 1;
+    }
+  };
   // Minimum of a group of counters: relaxed loads issued together, then one
   // acquire fence (an acquire per load would serialise the LDS round trips).
   auto counters_min = [&](const int* cnt, auto n_tag) {
@@ -552,7 +572,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     const int64_t slot = w_id + j;
     float* ms = mrg + hb * C::MSLOT;
     if (par == 1) {
-      spin_until_ge(&mrg_read[hb], seg);  // the previous segment's state has been taken
+      note(spin_until_ge(&mrg_read[hb], seg, a.spin_limit));  // the previous segment's state has been taken
       if (active) {
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db)
@@ -566,7 +586,8 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       if (lane == 0) publish(&mrg_written[hb], seg + 1);
       return;
     }
-    spin_until_ge(&mrg_written[hb], seg + 1);
+    note(spin_until_ge(&mrg_written[hb], seg + 1, a.spin_limit));
+    const bool poison = broken || __hip_atomic_load(&ring_broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (active) {
       const float mo = ms[16 * C::DBLK * 64 + lane];
       const float lo1 = ms[16 * C::DBLK * 64 + 64 + lane];
@@ -590,7 +611,8 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
           if (row < cc.rows) *reinterpret_cast<uint2*>(op + 32 * db + 8 * rr + 4 * g) = w2;
         }
       if (g == 0 && row < cc.rows)
-        a.part_lse[slot * C::ROWS + row] = l_tot > 0.0f ? (M + fast_log2(l_tot)) * kLn2 : kNegInf;
+        a.part_lse[slot * C::ROWS + row] =
+            poison ? __builtin_nanf("") : (l_tot > 0.0f ? (M + fast_log2(l_tot)) * kLn2 : kNegInf);
     }
     if (lane == 0) publish(&mrg_read[hb], seg + 1);  // the slot may be refilled
     if (lane == 0 && hb == 0 && job_end) a.job_seg[2 * j + 1] = w_id;  // this workgroup ends the job
@@ -621,8 +643,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       const int need = issued - C::NS + 1;  // the slot's previous item must be done
       // While the slot is busy, publish the oldest unpublished item one at a
       // time (the consumers may be waiting for it), else sleep.
-      for (int n = 0; seen < need && n < kSpinLimit; ++n) {
+      for (int n = 0; seen < need; ++n) {
         if ((seen = consumed_min()) >= need) break;
+        if (n >= a.spin_limit) {  // the slot may still be read: stale data for a consumer
+          note(false);
+          break;
+        }
         if (published < issued) {
           wait_items<C::PER, C::NS - 1>(issued - published - 1);
           ++published;
@@ -641,11 +667,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       }
     }
     publish_all();
+    if (broken) status_or(a.status, kDecodeStatusWait);
     return;
   }
   int seg = 0, have = 0;  // have: a lower bound of the landed count
   auto wait_landed = [&](int v) {
-    if (have < v) spin_until(([&] { return (have = landed_min()) >= v; }));
+    if (have < v) note(spin_until(([&] { return (have = landed_min()) >= v; }), a.spin_limit));
   };
   for (int i = 0; cc.left > 0;) {
     // The next group: a job's query items (read by every consumer wave), or
@@ -693,6 +720,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     for (int t = 0; t < gsz; ++t) advance(cc);
     i += gsz;
   }
+  if (broken) status_or(a.status, kDecodeStatusWait);
 }
 
 // Merge the partial results of one job: one thread per (head row, 4 columns).
@@ -717,8 +745,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int t = jr / G;
   const int h = g_kv * G + (jr - t * G);
   const int Lb = seq_len(a, b);
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
+    const int raw = a.seqlens[b];
+    if (raw < 0 || raw > a.Smax - a.len_add) status_or(a.status, kDecodeStatusLength);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float m = kNegInf, tot = 0.0f;
+  bool poisoned = false;  // a partial was written as NaN (an expired wait)
   if (Lb > 0) {
     const int w0 = a.job_seg[2 * j], w1 = a.job_seg[2 * j + 1];
     const float* pl = a.part_lse + ((int64_t)w0 + j) * ROWS + r;
@@ -737,7 +770,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       }
       float mr = m;
 #pragma unroll
-      for (int e = 0; e < U; ++e) mr = fmaxf(mr, ls[e]);
+      for (int e = 0; e < U; ++e) {
+        poisoned |= ls[e] != ls[e];
+        mr = fmaxf(mr, ls[e]);
+      }
       if (mr == kNegInf) continue;
       const float sc = m == kNegInf ? 0.0f : fast_exp2((m - mr) * kLog2e);
       tot *= sc;
@@ -757,14 +793,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       m = mr;
     }
   }
-  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+  float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+  if (poisoned) {
+    inv = __builtin_nanf("");
+    m = __builtin_nanf("");
+  }
   bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)t * a.o_ss + (int64_t)h * a.o_sh + 4 * d4;
   const uint32_t lo2 = (uint32_t)(f32_to_elem<T>(acc.x * inv)) |
                        ((uint32_t)(f32_to_elem<T>(acc.y * inv)) << 16);
   const uint32_t hi2 = (uint32_t)(f32_to_elem<T>(acc.z * inv)) |
                        ((uint32_t)(f32_to_elem<T>(acc.w * inv)) << 16);
   *reinterpret_cast<uint2*>(op) = make_uint2(lo2, hi2);
-  if (d4 == 0) a.lse[((int64_t)b * a.Hq + h) * a.Sq + t] = tot > 0.0f ? m + fast_log2(tot) * kLn2 : kNegInf;
+  if (d4 == 0)
+    a.lse[((int64_t)b * a.Hq + h) * a.Sq + t] = (tot > 0.0f || poisoned) ? m + fast_log2(tot) * kLn2 : kNegInf;
 }
 
 // In-place append: rows [L_b, L_b + len_add) of sequence b's cache (paged or
@@ -852,8 +893,9 @@ DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int part
   DecodeWorkspace w;
   const size_t jobs = (size_t)B * Hkv * decode_head_groups(Hq, Hkv, Sq);
   const size_t slots = (size_t)parts + jobs;
-  w.o_off = 0;
-  w.lse_off = (slots * kDecodeRows * D * sizeof(uint16_t) + 255) / 256 * 256;
+  w.status_off = 0;  // the status word; 256 bytes keep the rest aligned
+  w.o_off = 256;
+  w.lse_off = w.o_off + (slots * kDecodeRows * D * sizeof(uint16_t) + 255) / 256 * 256;
   w.seg_off = w.lse_off + (slots * kDecodeRows * sizeof(float) + 255) / 256 * 256;
   w.bytes = w.seg_off + (jobs * 2 * sizeof(int32_t) + 255) / 256 * 256;
   return w;

@@ -241,6 +241,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
   __shared__ int lds_doc0_[NG * C::BN];
   __shared__ int lds_doc1_[NG * C::BN];
   __shared__ int lds_gsync_[NG];  // arrivals of each group's waves at its step barriers
+  __shared__ int lds_broken_;     // a step barrier wait expired (results are poisoned)
 
   const int tid_wg = threadIdx.x;
   const int wave_wg = __builtin_amdgcn_readfirstlane(tid_wg >> 6);
@@ -394,6 +395,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     store_doc(B0{});
   }
   if (tid_wg < NG) lds_gsync_[tid_wg] = 0;
+  if (tid_wg == 0) lds_broken_ = 0;
   wait_dma();
   __syncthreads();
 
@@ -403,7 +405,10 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
   // work on the same SIMD.  The tile buffers are per group, so a group
   // barrier orders everything a step needs: copies landed before reads, and
   // reads of a buffer done before the next copy into it.
+  // The wait is bounded (a.spin_limit sleeps); if it expires the tiles may
+  // not have landed, so the workgroup's rows are written as NaN at the end.
   int nsync = 0;
+  bool broken = false;
   auto step_sync = [&]() __attribute__((always_inline)) {
     if constexpr (NG == 1) {
       __syncthreads();
@@ -411,10 +416,14 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
       ++nsync;
       if (lane == 0) __hip_atomic_fetch_add(&lds_gsync_[grp], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       const int target = C::WPG * nsync;
-      for (int n = 0; n < (1 << 22); ++n) {
+      for (int n = 0;; ++n) {
         const int v = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(&lds_gsync_[grp], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (v >= target) break;
+        if (n >= a.spin_limit) {
+          broken = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
     }
@@ -477,6 +486,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     // to group 0 through LDS; wave w of each group owns the same 32 rows.
     // The slots overlap group 0's tile buffers, and the step barriers are per
     // group, so first both groups must be past their last step.
+    if (broken) lds_broken_ = 1;
     __syncthreads();
     constexpr int SLOT = 64 * (16 * C::DBLK + 2);  // floats per wave
     static_assert(SLOT * 4 <= C::TB, "state slot fits one tile buffer");
@@ -493,6 +503,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     }
     __syncthreads();  // group 1's state is in LDS
     if (grp == 1) return;
+    broken = lds_broken_ != 0;
     const float mo = st[16 * C::DBLK * 64 + lane];
     const float lo = st[16 * C::DBLK * 64 + 64 + lane];
     const float M = fmaxf(m_run, mo);
@@ -515,7 +526,8 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + wave_xor32(l_run);
   if (q_ok) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (broken) inv = __builtin_nanf("");
     bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)my_q * a.o_ss + h * a.o_sh;
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) {
@@ -530,7 +542,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     }
     if (g == 0)
       a.lse[((int64_t)b * a.Hq + h) * a.Sq + my_q] =
-          l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+          broken ? __builtin_nanf("") : (l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf);
   }
 }
 

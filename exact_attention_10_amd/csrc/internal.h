@@ -42,7 +42,15 @@ struct FwdArgs {
   float softcap;             // 0 = off
   MaskArgs mask;
   TileLists tiles;
+  int spin_limit;            // bound of the in-kernel waits (sleeps); see attn_debug_set_spin_limit
 };
+
+// Bound on every in-kernel spin wait, in s_sleep rounds: the default (about
+// 2^22) only matters if a hand-over protocol were broken; a wait that
+// expires poisons its outputs (NaN) and, in the decode path, sets a status
+// bit.  Tests lower it through attn_debug_set_spin_limit.
+constexpr int kDefaultSpinLimit = 1 << 22;
+int spin_limit();
 
 // bf16 MFMA forward.  Tiles of 128 or 256 query rows x 64 keys (block-sparse
 // masks use 128-row tiles).
@@ -134,14 +142,19 @@ struct DecodeArgs {
   int len_add;
   const void* k_new; const void* v_new;
   int64_t kn_sb, kn_ss, kn_sh, vn_sb, vn_ss, vn_sh;
+  uint32_t* status;          // sticky status word in the workspace (bits ORed in)
+  int spin_limit;
 };
+// Bits of the decode status word.
+constexpr uint32_t kDecodeStatusLength = 1;  // a cache length was outside [0, Smax - s_new]
+constexpr uint32_t kDecodeStatusWait = 2;    // an in-kernel wait expired (rows poisoned with NaN)
 constexpr int kDecodeRows = 128;  // rows (query, head) per decode job
 // Number of workgroups: num_splits when > 0, else the device's compute units.
 int decode_parts(int num_splits);
 int device_cu_count();  // compute units of the current device (cached per device)
 int decode_head_groups(int Hq, int Hkv, int Sq);  // jobs per (sequence, kv head)
 struct DecodeWorkspace {
-  size_t o_off, lse_off, seg_off, bytes;
+  size_t status_off, o_off, lse_off, seg_off, bytes;
 };
 DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int parts);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);

@@ -136,10 +136,12 @@ typedef struct {
   int32_t B, Sq, Sk, Hq, Hkv, D;
   float softmax_scale;          /* NaN means 1/sqrt(D) (the page's None) */
   int32_t causal;               /* bottom-right aligned when Sq != Sk */
-  int32_t window_left;          /* -1 = unbounded */
-  int32_t window_right;         /* -1 = unbounded */
+  int32_t window_left;          /* -1 = unbounded; any side >= Sq + Sk
+                                   excludes nothing and is taken as -1 */
+  int32_t window_right;         /* -1 = unbounded (same rule) */
   const float* alibi_slopes;    /* device fp32, NULL = no ALiBi ([FA]:
-                                   (nheads,) or (batch, nheads)) */
+                                   (nheads,) or (batch, nheads): element
+                                   [b * alibi_batch_stride + h]) */
   int64_t alibi_batch_stride;   /* 0 for (Hq,), Hq for (B, Hq) */
   float softcap;                /* 0 = off; else softcap * tanh(s/softcap) */
   const attn_block_mask* block_mask;  /* NULL = dense; when given, causal
@@ -151,6 +153,17 @@ typedef struct {
 const char* attn_status_string(attn_status s);
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* attn_last_error(void);
+
+/* Testing hook: the bound, in sleep rounds, of every in-kernel wait of the
+ * forward and decode kernels for launches enqueued after the call (a value
+ * below 0 restores the default, about 4 million).  The bound is never reached
+ * when the kernels' hand-over protocols work; a wait that reaches it stops
+ * waiting, the kernel finishes normally, and the rows that may have read
+ * unsynchronised data are written as NaN (o and lse); the decode path also
+ * sets bit 2 of its status word (attn_decode).  With 0 the waits give up at
+ * once, which lets a test see that path without a broken kernel.  Host only;
+ * process-wide; never fails. */
+void attn_debug_set_spin_limit(int32_t limit);
 
 /* ---------------------------------------------------------------------
  * Forward ([TA] "Tiling the Computation", "2. Online Softmax",
@@ -267,14 +280,23 @@ attn_status attn_bwd_stage(const attn_params* p, attn_tensor q, attn_tensor k,
  *       ALiBi and block masks are not supported by this entry point
  *       (UNSUPPORTED).
  *   q : [B, Sq, Hq, D];  k_cache, v_cache : [B, Smax, Hkv, D].
- *   cache_seqlens : device int32 [B], each in [0, Smax] (values outside are
- *       clamped to that range on the device).  A sequence of length 0 gives
- *       o = 0 and lse = -inf.
+ *   cache_seqlens : device int32 [B], each in [0, Smax].  The lengths are read
+ *       on the device only: a value outside that range is clamped to it and
+ *       reported in the workspace status word (below).  A sequence of length
+ *       0 gives o = 0 and lse = -inf.
  *   num_splits : number of ranges (workgroups) the total key work is cut
  *       into; 0 = one per compute unit of the current device.  At most
  *       65536.  Any value gives the same result up to rounding.
  *   o : [B, Sq, Hq, D];  lse : fp32 [B, Hq, Sq] contiguous.
- *   workspace : at least attn_decode_workspace_size(p, num_splits) bytes.
+ *   workspace : at least attn_decode_workspace_size(p, num_splits) bytes,
+ *       256-byte aligned.  Its first 4 bytes are a sticky status word (uint32)
+ *       that the kernels only OR bits into and never clear: bit 1 = some
+ *       cache_seqlens[b] was outside [0, Smax - s_new] (s_new = 0 without an
+ *       append) and was clamped; bit 2 = an in-kernel wait reached its bound
+ *       (see attn_debug_set_spin_limit; the rows concerned are NaN).  The
+ *       caller zeroes the word (e.g. when allocating the workspace) and reads
+ *       it when it wants, after the stream has reached the call.  The rest of
+ *       the workspace is scratch.
  */
 attn_status attn_decode(const attn_params* p, attn_tensor q,
                         attn_tensor k_cache, attn_tensor v_cache,
@@ -297,9 +319,11 @@ size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits);
  *       sequence b uses batch row cache_batch_idx[b] of k_cache / v_cache,
  *       which then have cache_batch rows ([cache_batch, Sk, Hkv, D]); values
  *       are clamped to [0, cache_batch).
- *   k_new, v_new : [B, s_new, Hkv, D] bf16 (data NULL = no append).  Before
+ *   k_new, v_new : [B, s_new, Hkv, D] of q's dtype (bf16 or fp16; data NULL =
+ *       no append).  Before
  *       attending, rows [L_b, L_b + s_new) of each sequence's cache receive
- *       them (L_b = cache_seqlens[b], clamped to [0, Sk - s_new]) and the
+ *       them (L_b = cache_seqlens[b], clamped to [0, Sk - s_new], a clamp
+ *       reported by bit 1 of the workspace status word) and the
  *       queries then attend to L_b + s_new rows (with causal and
  *       Sq == s_new, query t sees the cache and the new rows up to t).  cache_seqlens is read, not
  *       advanced.  The caches are written in place (stream-ordered).

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libattn.so not 
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(?:attn_status|size_t|const char\*)\s+(\w+)\s*\(", text)
+    names = re.findall(r"\b(?:attn_status|size_t|const char\*|void)\s+(\w+)\s*\(", text)
     return sorted(set(names))
 
 

@@ -131,8 +131,9 @@ def test_bwd_block_sparse(b, case):
 def test_bwd_doc_mask_s8192(b):
     """The packed-document workload (B=2, H=16, S=8192, D=64, causal within
     documents, 128x128 blocks) through the block-sparse backward.  Documents
-    do not interact, so the oracle is run per document on four heads (the
-    pinned per-document identity) and compared with those slices."""
+    do not interact, so the oracle is run per document (the pinned
+    per-document identity) on all 16 heads, and every gradient element is
+    compared."""
     w = inputs.doc_mask()
     rng = np.random.default_rng(44)
     w["do"] = inputs.f32_to_bf16_bits(rng.standard_normal(w["q"].shape, dtype=np.float32))
@@ -140,8 +141,7 @@ def test_bwd_doc_mask_s8192(b):
     m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
     dq, dk, dv = run_bwd(b, w, softmax_scale=w["scale"], block_mask=m)
     got = [to_f64(t) for t in (dq, dk, dv)]
-    heads = [0, 5, 10, 15]
-    x = {n: f64(w, n)[:, :, heads] for n in ("q", "k", "v", "do")}
+    x = {n: f64(w, n) for n in ("q", "k", "v", "do")}
     for bb in range(2):
         s0 = 0
         for n in w["doc_lengths"][bb]:
@@ -150,8 +150,24 @@ def test_bwd_doc_mask_s8192(b):
                                        x["v"][bb:bb + 1, sl], x["do"][bb:bb + 1, sl],
                                        scale=w["scale"], causal=True)
             for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-                check_o(g[bb:bb + 1, sl][:, :, heads], r, GRAD_ATOL, "%s b%d doc@%d" % (name, bb, s0))
+                check_o(g[bb:bb + 1, sl], r, GRAD_ATOL, "%s b%d doc@%d" % (name, bb, s0))
             s0 += n
+        assert s0 == 8192
+
+
+def test_bwd_alibi_per_batch_slopes(b):
+    """Backward with ALiBi slopes of shape (batch, nheads) ("FlashAttention:
+    Fast and Memory-Efficient Exact Attention", "Examples"): every gradient
+    element against the oracle with the same per-batch table."""
+    B, S, Hq, Hkv, D = 3, 300, 4, 2, 128
+    w = inputs.random_case(71, B, S, S, Hq, Hkv, D, dtype="bf16", grad=True)
+    slopes = np.random.default_rng(72).uniform(0.05, 1.0, (B, Hq)).astype(np.float32)
+    kw = dict(softmax_scale=0.1, causal=True, window=(200, 0))
+    dq, dk, dv = run_bwd(b, w, alibi_slopes=torch.from_numpy(slopes).cuda(), **kw)
+    rq, rk, rv = oracle_grads(w, kw, slopes)
+    check_o(to_f64(dq), rq, GRAD_ATOL, "dQ")
+    check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
 
 
 def test_bwd_block_sparse_errors(b):

@@ -84,3 +84,82 @@ def test_decode_deterministic(b):
     o1, l1 = run_decode(b, w, softmax_scale=w["scale"])
     o2, l2 = run_decode(b, w, softmax_scale=w["scale"])
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_status_length_out_of_range(b):
+    """A cache length outside [0, Smax] is clamped on the device and reported
+    in bit 1 of the workspace status word (which the kernels never clear);
+    in-range lengths leave the word at 0.  Outputs follow the clamped
+    lengths."""
+    w = inputs.decode_mqa(seed=15, B=4, Hq=16, Smax=256, D=128, lmin=1, lmax=256)
+    q, k, v = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v"))
+    ws = torch.zeros(b.decode_workspace_size(q, k), dtype=torch.uint8, device="cuda")
+    lens = torch.tensor([10, 256, 3, 100], dtype=torch.int32, device="cuda")
+    b.attn_decode(q, k, v, lens, softmax_scale=0.1, workspace=ws)
+    assert b.decode_status(ws) == 0
+    bad = np.array([-5, 300, 3, 100], dtype=np.int32)
+    o, lse = b.attn_decode(q, k, v, torch.from_numpy(bad).cuda(), softmax_scale=0.1, workspace=ws)
+    torch.cuda.synchronize()
+    assert b.decode_status(ws) & 1
+    O, L = oracle.decode(f64(w, "q"), f64(w, "k"), f64(w, "v"), np.clip(bad, 0, 256), scale=0.1)
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    # sticky: a later clean call leaves the bit set until the caller clears it
+    b.attn_decode(q, k, v, lens, softmax_scale=0.1, workspace=ws)
+    assert b.decode_status(ws) & 1
+    ws.zero_()
+    b.attn_decode(q, k, v, lens, softmax_scale=0.1, workspace=ws)
+    assert b.decode_status(ws) == 0
+
+
+def test_decode_status_append_overflow(b):
+    """With an in-place append of s_new rows, a length above Smax - s_new is
+    clamped (the new rows then overwrite the last cached rows) and flagged."""
+    B, Hq, Hkv, D, Smax, s_new = 2, 8, 1, 128, 64, 4
+    w = inputs.decode_mqa(seed=16, B=B, Hq=Hq, Smax=Smax, D=D, lmin=1, lmax=Smax)
+    q, k, v = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v"))
+    rng = np.random.default_rng(17)
+    kn = torch.from_numpy(rng.standard_normal((B, s_new, Hkv, D), dtype=np.float32)).to(torch.bfloat16).cuda()
+    vn = torch.from_numpy(rng.standard_normal((B, s_new, Hkv, D), dtype=np.float32)).to(torch.bfloat16).cuda()
+    ws = torch.zeros(b.decode_workspace_size(q, k), dtype=torch.uint8, device="cuda")
+    lens = torch.tensor([Smax - s_new, 7], dtype=torch.int32, device="cuda")
+    b.attn_decode(q, k.clone(), v.clone(), lens, softmax_scale=0.1, k_new=kn, v_new=vn, workspace=ws)
+    torch.cuda.synchronize()
+    assert b.decode_status(ws) == 0
+    lens = torch.tensor([Smax - s_new + 1, 7], dtype=torch.int32, device="cuda")
+    b.attn_decode(q, k.clone(), v.clone(), lens, softmax_scale=0.1, k_new=kn, v_new=vn, workspace=ws)
+    torch.cuda.synchronize()
+    assert b.decode_status(ws) & 1
+
+
+def test_decode_expired_wait_poisons_rows(b):
+    """With the in-kernel wait bound at 0 (attn_debug_set_spin_limit) the
+    decode ring's waits give up: the kernels still finish, bit 2 of the
+    status word is set, the rows that may have read unsynchronised data are
+    NaN in o and lse, and every other row is still correct.  The default
+    bound gives a clean word and normal results again."""
+    w = inputs.decode_mqa()
+    q, k, v = (to_device(w[n], "bf16", torch) for n in ("q", "k", "v"))
+    lens = torch.from_numpy(np.asarray(w["cache_seqlens"], dtype=np.int32)).cuda()
+    ws = torch.zeros(b.decode_workspace_size(q, k), dtype=torch.uint8, device="cuda")
+    try:
+        b.set_spin_limit(0)
+        o, lse = b.attn_decode(q, k, v, lens, softmax_scale=w["scale"], workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        b.set_spin_limit(-1)
+    assert b.decode_status(ws) & 2
+    bad = torch.isnan(lse)  # [B, Hq, 1]
+    assert bad.any()
+    assert torch.equal(torch.isnan(o.float()).any(-1).permute(0, 2, 1), bad)
+    O, L = oracle.decode(f64(w, "q"), f64(w, "k"), f64(w, "v"), w["cache_seqlens"], scale=w["scale"])
+    good = (~bad).cpu().numpy()
+    on = to_f64(o).transpose(0, 2, 1, 3)[good]
+    check_o(on, O.transpose(0, 2, 1, 3)[good])
+    check_lse(to_f64(lse)[good], L[good])
+    ws.zero_()
+    o2, l2 = b.attn_decode(q, k, v, lens, softmax_scale=w["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    assert b.decode_status(ws) == 0
+    check_o(to_f64(o2), O)
+    check_lse(to_f64(l2), L)

@@ -151,10 +151,11 @@ def long_local():
 
 
 @pytest.mark.parametrize("mod", ["alibi", "softcap"])
-def test_fwd_long_local_sampled(b, long_local, mod):
-    """S=16384, causal + window (4096, 0), ALiBi or softcap 50: sampled rows of
-    8 heads (first/last rows, tile edges, window edge) against the oracle;
-    the tile trace of all heads against the closed-form tile classes."""
+def test_fwd_long_local_full(b, long_local, mod):
+    """S=16384, causal + window (4096, 0), ALiBi slopes 2^(-8(h+1)/32) or
+    softcap 50: every output row of every head against the oracle (which
+    restricts each row chunk to its window band), and the tile trace of all
+    heads against the closed-form tile classes."""
     w = long_local
     kw = dict(softmax_scale=w["scale"], causal=True, window=(4096, 0))
     slopes = None
@@ -166,16 +167,110 @@ def test_fwd_long_local_sampled(b, long_local, mod):
     o, lse, tr = run_fwd(b, w, trace=True, **kw)
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()
-    q, k, v = f64(w, "q"), f64(w, "k"), f64(w, "v")
-    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 4096, 4097, 8191, 8192, 12345, 16320, 16383])
-    for h in (0, 5, 10, 15, 16, 21, 27, 31):
-        Or, Lr = oracle.attention_fwd_rows(q, k, v, 0, h, rows, scale=w["scale"], causal=True,
-                                           window=(4096, 0), alibi_slopes=slopes,
-                                           softcap=kw.get("softcap", 0.0))
-        check_o(o[0, rows, h], Or, what="O[h=%d]" % h)
-        check_lse(lse[0, h, rows], Lr)
     exp = expected_trace(1, 32, 16384, 16384, *tr.tile, True, (4096, 0))
     np.testing.assert_array_equal(tr.cpu().numpy(), exp)
+    q, k, v = f64(w, "q"), f64(w, "k"), f64(w, "v")
+    rows = np.arange(16384)
+    for h in range(32):
+        for r0 in range(0, 16384, 2048):
+            rr = rows[r0:r0 + 2048]
+            Or, Lr = oracle.attention_fwd_rows(q, k, v, 0, h, rr, scale=w["scale"], causal=True,
+                                               window=(4096, 0), alibi_slopes=slopes,
+                                               softcap=kw.get("softcap", 0.0))
+            check_o(o[0, rr, h], Or, what="O[h=%d, rows %d..]" % (h, r0))
+            check_lse(lse[0, h, rr], Lr)
+
+
+WIDE_MOD_CASES = [
+    # enough causal tiles for 256-row workgroups, with score modifiers
+    (16, 512, 32, 8, 128, {"alibi": True}),
+    (16, 512, 32, 8, 128, {"softcap": 50.0}),
+    (32, 512, 32, 32, 64, {"alibi": True, "softcap": 4.0}),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_MOD_CASES, ids=[str(i) for i in range(len(WIDE_MOD_CASES))])
+def test_fwd_wide_tiles_causal_mods(b, case):
+    """Causal grids large enough for the 256-row kernel, with ALiBi and/or
+    softcap: every output against the oracle and the trace at the reported
+    tile shape (256 rows)."""
+    B, S, Hq, Hkv, D, opt = case
+    w = inputs.random_case(900 + B + D, B, S, S, Hq, Hkv, D, dtype="bf16")
+    scale = 0.09 if D == 128 else 0.13
+    kw = dict(softmax_scale=scale, causal=True, softcap=opt.get("softcap", 0.0))
+    slopes = None
+    if opt.get("alibi"):
+        slopes = np.exp2(-8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+    o, lse, tr = run_fwd(b, w, trace=True, **kw)
+    assert tr.tile == (256, 64)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=scale, causal=True,
+                                alibi_slopes=slopes, softcap=kw["softcap"])
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    np.testing.assert_array_equal(tr.cpu().numpy(), expected_trace(B, Hq, S, S, 256, 64, True))
+
+
+def test_fwd_alibi_per_batch_slopes(b):
+    """ALiBi slopes of shape (batch, nheads) ("FlashAttention: Fast and
+    Memory-Efficient Exact Attention", "Examples"): every batch row has its
+    own slopes; every output against the oracle, and the result differs from
+    using batch row 0's slopes everywhere."""
+    B, S, Hq, Hkv, D = 3, 300, 4, 2, 128
+    w = inputs.random_case(61, B, S, S, Hq, Hkv, D, dtype="bf16")
+    slopes = np.random.default_rng(62).uniform(0.05, 1.0, (B, Hq)).astype(np.float32)
+    kw = dict(softmax_scale=0.1, causal=True, window=(200, 0))
+    o, lse, _ = run_fwd(b, w, alibi_slopes=torch.from_numpy(slopes).cuda(), **kw)
+    O, L = oracle.attention_fwd(f64(w, "q"), f64(w, "k"), f64(w, "v"), scale=0.1, causal=True,
+                                window=(200, 0), alibi_slopes=slopes)
+    check_o(to_f64(o), O)
+    check_lse(to_f64(lse), L)
+    o1, _, _ = run_fwd(b, w, alibi_slopes=torch.from_numpy(slopes[0].copy()).cuda(), **kw)
+    assert (o1[1:].float() - o[1:].float()).abs().max().item() > 1e-2
+
+
+def test_fwd_huge_window_is_unbounded(b):
+    """A window side of 2^31 - 1 excludes no key: window (2^31 - 1, 0) with
+    causal gives exactly the causal result (bitwise), and the block mask
+    built with it equals the causal block mask."""
+    w = inputs.random_case(63, 1, 384, 384, 8, 2, 128, dtype="bf16")
+    big = 2 ** 31 - 1
+    o1, l1, _ = run_fwd(b, w, softmax_scale=0.1, causal=True)
+    o2, l2, _ = run_fwd(b, w, softmax_scale=0.1, causal=True, window=(big, 0))
+    o3, l3, _ = run_fwd(b, w, softmax_scale=0.1, causal=False, window=(big, big))
+    o4, l4, _ = run_fwd(b, w, softmax_scale=0.1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+    m1 = b.block_mask_build(1, 384, 384, 128, 128, causal=True)
+    m2 = b.block_mask_build(1, 384, 384, 128, 128, causal=True, window=(big, big))
+    for name, arr in m1.arrays().items():
+        assert torch.equal(arr, m2.arrays()[name]), name
+
+
+def test_fwd_expired_wait_poisons_rows(b):
+    """With the in-kernel wait bound set to 0 (attn_debug_set_spin_limit),
+    the two-group forward kernel stops waiting at its group barriers: the
+    kernel still finishes, and every workgroup in which a wait gave up writes
+    its rows as NaN; every other row is still correct.  The default bound
+    restores bitwise-normal results."""
+    B, S, Hq, Hkv, D = 1, 1000, 8, 2, 128
+    w = inputs.random_case(64, B, S, S, Hq, Hkv, D, dtype="bf16")
+    o_ref, l_ref, _ = run_fwd(b, w, softmax_scale=0.1, causal=True)
+    try:
+        b.set_spin_limit(0)
+        o, lse, _ = run_fwd(b, w, softmax_scale=0.1, causal=True)
+    finally:
+        b.set_spin_limit(-1)
+    bad = torch.isnan(lse)
+    assert bad.any(), "no wait expired with a zero bound"
+    # a poisoned row is NaN in O as well; the others equal the normal run
+    ob = torch.isnan(o.float()).any(-1).permute(0, 2, 1)
+    assert torch.equal(ob, bad)
+    good = ~bad
+    assert torch.equal(lse[good], l_ref[good])
+    assert torch.equal(o.permute(0, 2, 1, 3)[good], o_ref.permute(0, 2, 1, 3)[good])
+    o2, l2, _ = run_fwd(b, w, softmax_scale=0.1, causal=True)
+    assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref)
 
 
 @pytest.fixture(scope="module")
@@ -208,26 +303,29 @@ def test_block_mask_device_small(b, shape):
 
 
 def test_fwd_doc_block_sparse(b, doc_mask):
-    """Block-sparse document mask forward: sampled rows of every head against
-    the oracle; visited tiles (trace) equal to the non-empty mask tiles."""
+    """Block-sparse document mask forward (B=2, H=16, S=8192, D=64): every
+    output of every head against the oracle, run per document (documents do
+    not interact: the pinned per-document identity); visited tiles (trace)
+    equal to the non-empty mask tiles."""
     w = doc_mask
     doc = torch.from_numpy(w["doc"]).cuda()
     m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
     o, lse, tr = run_fwd(b, w, trace=True, softmax_scale=w["scale"], block_mask=m)
+    exp = expected_trace(2, 16, 8192, 8192, 128, 128, True, doc=w["doc"])
+    np.testing.assert_array_equal(tr.cpu().numpy(), exp)
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()
     q, k, v = f64(w, "q"), f64(w, "k"), f64(w, "v")
     for bb in range(2):
-        rows = np.unique(np.concatenate([[0, 1, 127, 128, 4000, 8191],
-                                         np.cumsum(w["doc_lengths"][bb])[:-1],
-                                         np.cumsum(w["doc_lengths"][bb])[:-1] - 1]))
-        for h in range(0, 16, 3):
-            Or, Lr = oracle.attention_fwd_rows(q, k, v, bb, h, rows, scale=w["scale"],
-                                               causal=True, doc_q=w["doc"], doc_k=w["doc"])
-            check_o(o[bb, rows, h], Or)
-            check_lse(lse[bb, h, rows], Lr)
-    exp = expected_trace(2, 16, 8192, 8192, 128, 128, True, doc=w["doc"])
-    np.testing.assert_array_equal(tr.cpu().numpy(), exp)
+        s0 = 0
+        for n in w["doc_lengths"][bb]:
+            sl = slice(s0, s0 + n)
+            Or, Lr = oracle.attention_fwd(q[bb:bb + 1, sl], k[bb:bb + 1, sl], v[bb:bb + 1, sl],
+                                          scale=w["scale"], causal=True)
+            check_o(o[bb:bb + 1, sl], Or, what="O b%d doc@%d" % (bb, s0))
+            check_lse(lse[bb:bb + 1, :, sl], Lr)
+            s0 += n
+        assert s0 == 8192
 
 
 def test_fwd_doc_block_sparse_small_full(b):

@@ -67,7 +67,9 @@ def brute_fwd(q, k, v, scale, causal=False, window=(-1, -1), slopes=None,
                     if softcap > 0:
                         s = softcap * math.tanh(s / softcap)
                     if slopes is not None:
-                        s -= float(slopes[h]) * abs(i + (Sk - Sq) - j)
+                        # (Hq,) slopes, or (B, Hq): one row per batch row
+                        a = slopes[h] if np.ndim(slopes) == 1 else slopes[b][h]
+                        s -= float(a) * abs(i + (Sk - Sq) - j)
                     us.append((j, s))
                 if not us:
                     continue
@@ -94,6 +96,8 @@ def brute_fwd(q, k, v, scale, causal=False, window=(-1, -1), slopes=None,
     dict(softcap=1.5),
     dict(slopes=True),
     dict(slopes=True, softcap=2.0, causal=True),
+    dict(slopes2d=True, causal=True),
+    dict(slopes2d=True, window=(3, 2)),
     dict(doc=True, causal=True),
     dict(kv_len=4),
 ])
@@ -114,6 +118,11 @@ def test_fwd_matches_brute_force(case, shape):
         kw.update(doc_q=doc, doc_k=doc)
     if case.get("slopes"):
         slopes = rng.uniform(0.1, 1.0, Hq)
+        kw["alibi_slopes"] = slopes
+    if case.get("slopes2d"):
+        # per-batch slopes [B, Hq]; every entry distinct, so a swapped
+        # [h, b] index or a flattened-index slip changes the result
+        slopes = rng.uniform(0.1, 1.0, (B, Hq)) + 0.01 * np.arange(B * Hq).reshape(B, Hq)
         kw["alibi_slopes"] = slopes
     for name in ("causal", "window", "softcap", "kv_len"):
         if name in case:
@@ -299,6 +308,60 @@ def test_alibi_sign_and_symmetry_noncausal():
         assert L[0, 0, i] < math.log(S)
 
 
+def test_alibi_per_batch_slopes_are_per_row_runs():
+    """ALiBi slopes of shape (batch, nheads) ([FA] "Examples": alibi_slopes
+    is (nheads,) or (batch_size, nheads)): batch row b uses row b of the
+    table, so the result equals running each batch row alone with that 1-D
+    row.  Forward and gradients, with rows that differ per batch and per
+    head, and an [h, b] transposition must not pass."""
+    rng = np.random.default_rng(21)
+    B, Sq, Sk, Hq, Hkv, D = 3, 7, 9, 4, 2, 5
+    q, k, v, do = (rng.standard_normal(s) for s in
+                   [(B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D), (B, Sq, Hq, D)])
+    slopes = rng.uniform(0.05, 1.5, (B, Hq))
+    kw = dict(scale=0.6, causal=True, window=(5, 0))
+    O, L = oracle.attention_fwd(q, k, v, alibi_slopes=slopes, **kw)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, alibi_slopes=slopes, **kw)
+    for b in range(B):
+        sl = slice(b, b + 1)
+        Ob, Lb = oracle.attention_fwd(q[sl], k[sl], v[sl], alibi_slopes=slopes[b], **kw)
+        np.testing.assert_allclose(O[sl], Ob, atol=1e-14)
+        np.testing.assert_allclose(L[sl], Lb, rtol=1e-14)
+        eq, ek, ev = oracle.attention_bwd(q[sl], k[sl], v[sl], do[sl], alibi_slopes=slopes[b], **kw)
+        np.testing.assert_allclose(dq[sl], eq, atol=1e-14)
+        np.testing.assert_allclose(dk[sl], ek, atol=1e-14)
+        np.testing.assert_allclose(dv[sl], ev, atol=1e-14)
+    # rows taken in another batch order give a different answer (the
+    # comparison above can see a batch-index slip)
+    Ox, _ = oracle.attention_fwd(q, k, v, alibi_slopes=slopes[::-1], **kw)
+    assert np.abs(Ox - O).max() > 1e-3
+    # decode takes the same table: batch row b of a (B, Hq) table
+    Od, Ld = oracle.decode(q[:, -1:], k, v, np.array([9, 4, 7]), scale=0.6,
+                           alibi_slopes=slopes)
+    for b, n in enumerate((9, 4, 7)):
+        ob, lb = oracle.attention_fwd(q[b:b + 1, -1:], k[b:b + 1, :n], v[b:b + 1, :n],
+                                      scale=0.6, alibi_slopes=slopes[b])
+        np.testing.assert_allclose(Od[b], ob[0], atol=1e-14)
+        np.testing.assert_allclose(Ld[b], lb[0], rtol=1e-14)
+
+
+def test_alibi_per_batch_brute_force_values():
+    """Per-batch ALiBi against hand-countable values: Q = 0, causal, slope
+    table a[b, h]: LSE of row i is the geometric series
+    log((1 - e^{-a n}) / (1 - e^{-a})) with n = i + 1 and a = a[b, h]."""
+    S = 12
+    a = np.array([[0.2, 0.9], [1.3, 0.05]])
+    q = np.zeros((2, S, 2, 3))
+    k, v = rand(2, S, 1, 3), rand(2, S, 1, 3)
+    _, L = oracle.attention_fwd(q, k, v, scale=1.0, causal=True, alibi_slopes=a)
+    for b in range(2):
+        for h in range(2):
+            for i in range(S):
+                n = i + 1
+                expect = math.log((1 - math.exp(-a[b, h] * n)) / (1 - math.exp(-a[b, h])))
+                assert abs(L[b, h, i] - expect) < 1e-13
+
+
 def test_softcap_limits():
     """[P11] Softcap c: (a) Q = 0 is unaffected; (b) c -> infinity is no
     softcap; (c) tiny c squashes every score into (-c, c), so the output is the
@@ -364,6 +427,7 @@ def _loss(q, k, v, do, kw):
     dict(scale=0.5, window=(1, 2), alibi_slopes=np.array([0.3, 0.6, 0.2, 0.9])),
     dict(scale=0.9, causal=True, softcap=1.3),
     dict(scale=0.8, causal=True, doc=True),
+    dict(scale=0.6, causal=True, alibi2d=True),
 ])
 def test_bwd_finite_differences(kw):
     """[P12] Central differences of L = sum(O * dO) in fp64 on a tiny GQA
@@ -376,6 +440,12 @@ def test_bwd_finite_differences(kw):
     if kw.pop("doc", False):
         doc = np.array([[0, 0, 1, 1, 1, 2]])
         kw.update(doc_q=doc, doc_k=doc)
+    if kw.pop("alibi2d", False):
+        # two batch rows with their own (B, Hq) slope rows
+        B = 2
+        q, k, v, do = (rng.standard_normal(s) for s in
+                       [(B, Sq, Hq, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D), (B, Sq, Hq, D)])
+        kw["alibi_slopes"] = np.array([[0.3, 0.6, 0.2, 0.9], [1.1, 0.05, 0.7, 0.4]])
     dq, dk, dv = oracle.attention_bwd(q, k, v, do, row_chunk=4, **kw)
     eps = 1e-6
     for x, gx in ((q, dq), (k, dk), (v, dv)):
@@ -618,6 +688,23 @@ def test_unmasked_fractions():
     n = oracle.allowed_pair_count(16384, 16384, causal=True, window=(4096, 0), row_chunk=2048)
     # rows i < 4096 see i + 1 keys, later rows see 4097
     assert n == 4096 * 4097 // 2 + (16384 - 4096) * 4097 == 58734592
+
+
+@pytest.mark.parametrize("L", [0, 1, 5, 8, 9, 12])
+def test_cache_length_predicate_counts(L):
+    """The cache-length term of the predicate ([FA] "Examples",
+    cache_seqlens: only the first L cached rows are attended): every row of
+    a non-causal Sq x Sk problem sees exactly min(L, Sk) keys, namely keys
+    0 .. min(L, Sk) - 1; with causal (bottom-right) row i sees
+    min(L, i + Sk - Sq + 1) keys."""
+    Sq, Sk = 4, 9
+    ok = oracle.allowed_mask(np.arange(Sq), np.arange(Sk), Sq, Sk, kv_len=L)
+    assert np.array_equal(ok.sum(1), np.full(Sq, min(L, Sk)))
+    assert np.array_equal(np.nonzero(ok[0])[0], np.arange(min(L, Sk)))
+    assert oracle.allowed_pair_count(Sq, Sk, kv_len=L) == Sq * min(L, Sk)
+    okc = oracle.allowed_mask(np.arange(Sq), np.arange(Sk), Sq, Sk, causal=True, kv_len=L)
+    for i in range(Sq):
+        assert okc[i].sum() == max(0, min(L, i + Sk - Sq + 1))
 
 
 def test_seeded_workload_side_data():
