@@ -24,9 +24,13 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file flags (none at present; kept so a translation unit can get its own).
+FILE_FLAGS = {}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
