@@ -125,6 +125,12 @@ _lib.block_mask_build.argtypes = [_P(attn_mask_desc), ctypes.c_int32, ctypes.c_i
                                   ctypes.c_void_p, ctypes.c_size_t, _P(attn_block_mask),
                                   ctypes.c_void_p]
 
+_lib.attn_decode_noalloc.restype = ctypes.c_int
+_lib.attn_decode_noalloc.argtypes = [_P(attn_params), attn_tensor, attn_tensor, attn_tensor,
+                                     ctypes.c_void_p, ctypes.c_int32, attn_tensor,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.attn_decode_noalloc_max_bytes.restype = ctypes.c_size_t
+_lib.attn_decode_noalloc_max_bytes.argtypes = []
 _lib.attn_debug_set_spin_limit.restype = None
 _lib.attn_debug_set_spin_limit.argtypes = [ctypes.c_int32]
 
@@ -132,7 +138,8 @@ EXPORTED = ["attn_status_string", "attn_last_error", "attn_debug_set_spin_limit"
             "attn_fwd", "attn_fwd_tile_shape",
             "attn_fwd_workspace_size",
             "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_size", "attn_decode",
-            "attn_decode_kvcache", "attn_decode_workspace_size", "attn_block_mask_bytes",
+            "attn_decode_kvcache", "attn_decode_workspace_size", "attn_decode_noalloc",
+            "attn_decode_noalloc_max_bytes", "attn_block_mask_bytes",
             "block_mask_build"]
 
 
@@ -551,6 +558,41 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, softmax_scale=None, softcap=
                                         int(num_splits), _tensor(out), _ptr(lse), _ptr(workspace),
                                         workspace.numel(), _stream()))
     return out, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse, softmax_scale=None,
+                        softcap=0.0, num_splits=0, causal=False, status=None):
+    """attn_decode without a workspace (the library's per-device scratch):
+    out and lse are caller-provided, nothing is allocated.  status: None or
+    a device int32 tensor of one element receiving the sticky status bits."""
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q and the caches must be 4-d tensors")
+    B, Sq, Hq, D = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("k_cache must be [B=%d, Smax, Hkv, D=%d], got %s" % (B, D, _shape_of(k_cache)))
+    _check_like("v_cache", v_cache, k_cache)
+    _need_dtype("k_cache", k_cache, q.dtype)
+    _need_shape("cache_seqlens", cache_seqlens, (B,))
+    _need_dtype("cache_seqlens", cache_seqlens, torch.int32)
+    _need_contig("cache_seqlens", cache_seqlens)
+    if out is None or lse is None:
+        raise ValueError("attn_decode_noalloc writes into caller-provided out and lse")
+    _check_like("out", out, q)
+    _check_lse(lse, B, Hq, Sq)
+    if status is not None:
+        if status.numel() != 1 or status.dtype != torch.int32:
+            raise ValueError("status must be a one-element int32 tensor")
+    _need_device(q, k_cache=k_cache, v_cache=v_cache, cache_seqlens=cache_seqlens, out=out,
+                 lse=lse, status=status)
+    p = _params(q, k_cache, D, softmax_scale, causal, (-1, -1), None, softcap, None)
+    _check(_lib.attn_decode_noalloc(ctypes.byref(p), _tensor(q), _tensor(k_cache), _tensor(v_cache),
+                                    _ptr(cache_seqlens), int(num_splits), _tensor(out), _ptr(lse),
+                                    _ptr(status), _stream()))
+    return out, lse
+
+
+def decode_noalloc_max_bytes():
+    return _lib.attn_decode_noalloc_max_bytes()
 
 
 def decode_status(workspace):

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "internal.h"
@@ -373,7 +374,8 @@ size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits) {
 static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor k_cache,
                                attn_tensor v_cache, const int32_t* cache_seqlens,
                                const attn_kvcache* kv, int32_t num_splits, attn_tensor o, float* lse,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               uint32_t* status = nullptr, const char* scratch_name = nullptr) {
   g_err[0] = 0;
   Common cm;
   attn_status st = check_params(p, &cm);
@@ -422,6 +424,11 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
     return fail(ATTN_ERR_INVALID_ARG, "num_splits must be in [0, 65536] (got %d)", num_splits);
   if (p->B == 0) return ATTN_OK;
   const size_t need = attn_decode_workspace_size(p, num_splits);
+  if (scratch_name != nullptr && need > workspace_bytes)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "this decode needs %zu bytes of scratch; %s holds at most %zu (use attn_decode "
+                "with a caller workspace, or fewer splits / sequences)",
+                need, scratch_name, workspace_bytes);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "attn_decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
@@ -464,7 +471,7 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
   a.nhg = attn::decode_head_groups(p->Hq, p->Hkv, p->Sq);
   const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->Sq, p->D, a.parts);
   char* wsb = static_cast<char*>(workspace);
-  a.status = reinterpret_cast<uint32_t*>(wsb + wl.status_off);
+  a.status = status != nullptr ? status : reinterpret_cast<uint32_t*>(wsb + wl.status_off);
   a.spin_limit = attn::spin_limit();
   a.part_o = reinterpret_cast<uint16_t*>(wsb + wl.o_off);
   a.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
@@ -478,6 +485,62 @@ attn_status attn_decode(const attn_params* p, attn_tensor q, attn_tensor k_cache
                         void* stream) {
   return decode_impl(p, q, k_cache, v_cache, cache_seqlens, nullptr, num_splits, o, lse, workspace,
                      workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode without allocation or caller workspace (attn_decode_noalloc).  Its
+// scratch is this file-scope device array: each GPU the library runs on
+// holds one copy for the life of the process.  In host code `scratch` names
+// a host-side stand-in, not the device copy, so its device address is looked
+// up once per device with hipGetSymbolAddress and only that address is
+// handed to kernels.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;  // 64 MiB per GPU
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of `scratch` (looked up on
+// the first call on that device).
+attn_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+attn_status attn_decode_noalloc(const attn_params* p, attn_tensor q, attn_tensor k_cache,
+                                attn_tensor v_cache, const int32_t* cache_seqlens,
+                                int32_t num_splits, attn_tensor o, float* lse, uint32_t* status,
+                                void* stream) {
+  g_err[0] = 0;
+  void* ws = nullptr;
+  attn_status st = scratch_for_current_device(&ws);
+  if (st != ATTN_OK) return st;
+  return decode_impl(p, q, k_cache, v_cache, cache_seqlens, nullptr, num_splits, o, lse, ws,
+                     kNoAllocScratchBytes, stream, status, "attn_decode_noalloc's device scratch");
 }
 
 attn_status attn_decode_kvcache(const attn_params* p, attn_tensor q, attn_tensor k_cache,

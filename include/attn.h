@@ -306,6 +306,35 @@ attn_status attn_decode(const attn_params* p, attn_tensor q,
 size_t attn_decode_workspace_size(const attn_params* p, int32_t num_splits);
 
 /* ---------------------------------------------------------------------
+ * attn_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same computation, arguments, kernels and results as
+ * attn_decode (bitwise, for the same num_splits), except:
+ *   - the scratch is a device array inside the library, 64 MiB on each GPU
+ *     it runs on (held until the process ends; attn_decode_noalloc_max_bytes()
+ *     returns the size).  A problem whose attn_decode_workspace_size exceeds
+ *     it is rejected with ATTN_ERR_UNSUPPORTED before anything is enqueued.
+ *   - status : NULL, or a caller-owned device uint32 that receives the
+ *     sticky status bits attn_decode writes into its workspace word (1 = a
+ *     cache length was clamped, 2 = an in-kernel wait reached its bound);
+ *     the library never clears it.
+ *   - the scratch of the current device is shared by every call on that
+ *     device: calls that may overlap on one GPU (different streams, or
+ *     threads) race and must be serialised by the caller.  Nothing in the
+ *     scratch needs clearing between calls (every value is written before it
+ *     is read within a call).
+ * The current device must be the device of the tensors and the stream.  The
+ * call allocates and frees nothing (no hipMalloc / hipFree, no allocating
+ * library routine); the first call on a device looks the scratch up with
+ * hipGetSymbolAddress, which does not allocate. */
+attn_status attn_decode_noalloc(const attn_params* p, attn_tensor q,
+                                attn_tensor k_cache, attn_tensor v_cache,
+                                const int32_t* cache_seqlens, int32_t num_splits,
+                                attn_tensor o, float* lse, uint32_t* status,
+                                void* stream);
+size_t attn_decode_noalloc_max_bytes(void);
+
+/* ---------------------------------------------------------------------
  * Decode over a paged and/or batch-indexed KV cache with in-place append
  * ([FA] flash_attn_with_kvcache: "k_cache, v_cache: cached keys/values,
  * updated inplace", arguments k, v, cache_batch_idx, block_table).
