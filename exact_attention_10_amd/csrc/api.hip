@@ -573,6 +573,9 @@ attn_status block_mask_build(const attn_mask_desc* m, int32_t B, int32_t Sq, int
     return fail(ATTN_ERR_INVALID_ARG, "window sides must be >= -1");
   if ((m->doc_q == nullptr) != (m->doc_k == nullptr))
     return fail(ATTN_ERR_INVALID_ARG, "give both doc_q and doc_k or neither");
+  if (m->doc_q != nullptr && (block_m > attn::block_mask_max_block() || block_n > attn::block_mask_max_block()))
+    return fail(ATTN_ERR_UNSUPPORTED, "with document ids the block size is at most %d (got %dx%d)",
+                attn::block_mask_max_block(), block_m, block_n);
   const size_t need = attn_block_mask_bytes(B, Sq, Sk, block_m, block_n);
   if (buffer == nullptr || buffer_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "block mask needs %zu bytes, got %zu", need, buffer_bytes);

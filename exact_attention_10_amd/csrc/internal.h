@@ -169,5 +169,6 @@ struct BlockMaskArgs {
   int32_t* q_num_full; int32_t* q_idx_full;
 };
 hipError_t launch_block_mask(const BlockMaskArgs& a, hipStream_t s);
+int block_mask_max_block();  // largest block_m / block_n with a document mask
 
 }  // namespace attn

@@ -378,14 +378,20 @@ attn_status attn_decode_kvcache(const attn_params* p, attn_tensor q, attn_tensor
 /* ---------------------------------------------------------------------
  * Block-mask construction on the device ([GYM] create_block_mask with
  * BLOCK_SIZE; [FX4] block-sparse masks skip tiles with nothing to compute).
- * Classifies every tile by evaluating the predicate of `m` on every in-bounds
- * pair of the tile (a tile crossing the end of the sequence is never FULL),
- * then writes the ascending CSR lists (forward and transposed).
+ * Classifies every tile exactly as if the predicate of `m` were evaluated on
+ * every in-bounds pair of the tile (a tile crossing the end of the sequence
+ * is never FULL): the causal / window part in closed form from the tile's
+ * corner rows, document ids compared once per tile edge (a tile holding a
+ * single document on each side) or, where a document boundary crosses the
+ * tile, pair by pair; then writes the ascending CSR lists (forward and
+ * transposed).  Any int32 document ids are accepted (they need not be
+ * sorted or contiguous).
  *   buffer : device memory of at least attn_block_mask_bytes(...) bytes,
  *            256-byte aligned; `out` (host struct) receives the header and
  *            pointers into it.
  * Errors: INVALID_ARG for non-positive sizes, window < -1, only one of
- * doc_q / doc_k given; WORKSPACE if the buffer is too small. */
+ * doc_q / doc_k given; UNSUPPORTED for block_m or block_n above 1024 with
+ * document ids; WORKSPACE if the buffer is too small. */
 size_t attn_block_mask_bytes(int32_t B, int32_t Sq, int32_t Sk,
                              int32_t block_m, int32_t block_n);
 attn_status block_mask_build(const attn_mask_desc* m, int32_t B, int32_t Sq,

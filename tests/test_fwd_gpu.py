@@ -302,6 +302,35 @@ def test_block_mask_device_small(b, shape):
         np.testing.assert_array_equal(got[name], arr, err_msg=name)
 
 
+@pytest.mark.parametrize("shape", [(2, 1000, 1000, 128, 128, 3), (1, 700, 900, 256, 64, 2),
+                                   (3, 333, 333, 64, 192, 40)])
+def test_block_mask_device_any_doc_ids(b, shape):
+    """Document ids that are not contiguous runs (random ids from a small
+    set, so nearly every tile mixes documents; and random runs of length up
+    to 40): every array bit-exact against the oracle's brute-force
+    classification, with causal on and off and a window."""
+    B, Sq, Sk, bm, bn, nd = shape
+    rng = np.random.default_rng(Sq + bn)
+    if nd > 10:  # runs of random lengths with random (repeating) ids
+        def runs(n):
+            out = []
+            while len(out) < n:
+                out += [int(rng.integers(0, 5))] * int(rng.integers(1, nd + 1))
+            return out[:n]
+        dq = np.array([runs(Sq) for _ in range(B)], dtype=np.int32)
+        dk = np.array([runs(Sk) for _ in range(B)], dtype=np.int32)
+    else:
+        dq = rng.integers(0, nd, (B, Sq)).astype(np.int32)
+        dk = rng.integers(0, nd, (B, Sk)).astype(np.int32)
+    for causal, window in ((True, (-1, -1)), (False, (-1, -1)), (False, (150, 20))):
+        m = b.block_mask_build(B, Sq, Sk, bm, bn, causal=causal, window=window,
+                               doc_q=torch.from_numpy(dq).cuda(), doc_k=torch.from_numpy(dk).cuda())
+        got = {k2: v2.cpu().numpy() for k2, v2 in m.arrays().items()}
+        exp = oracle.block_mask(B, Sq, Sk, bm, bn, causal=causal, window=window, doc_q=dq, doc_k=dk)
+        for name, arr in exp.items():
+            np.testing.assert_array_equal(got[name], arr, err_msg="%s causal=%s window=%s" % (name, causal, window))
+
+
 def test_fwd_doc_block_sparse(b, doc_mask):
     """Block-sparse document mask forward (B=2, H=16, S=8192, D=64): every
     output of every head against the oracle, run per document (documents do
