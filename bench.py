@@ -23,8 +23,9 @@ Besides the headline line the JSON carries:
                 through a random block table), long-context local attention
                 with ALiBi / softcap, the packed-document block-sparse mask
                 (device mask build and forward);
-  cpu_baseline  the fp64 CPU oracle timed on this host on one full step of the
-                same workload.
+  cpu_baseline  the fp64 CPU oracle timed on this host's cores: one full step
+                of the same workload (value) and every other workload
+                (per_config), with the core count, CPU model and BLAS.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
                        [--no-cpu-baseline] [--copy-calibration]
@@ -157,8 +158,11 @@ def main():
     launches = [("fwd", fwd)] + list(zip(["bwd_dq", "bwd_dkdv", "bwd_group_sum", "bwd_stage3"], stages))
     # Contractions each kernel executes per allowed pair and head (recomputed
     # products included): forward QK^T, PV; dK/dV: QK^T, dO V^T, P^T dO,
-    # dS^T Q; dQ: QK^T, dO V^T, dS K.
+    # dS^T Q; dQ: QK^T, dO V^T, dS K.  Of the backward's five counted
+    # contractions (QK^T, dO V^T, P^T dO, dS^T Q, dS K) dK/dV is credited the
+    # first four and dQ only dS K (its QK^T and dO V^T are recomputation).
     kernel_flops = {"fwd": fwd_flops, "bwd_dkdv": 2.0 * fwd_flops, "bwd_dq": 1.5 * fwd_flops}
+    kernel_flops_counted = {"fwd": fwd_flops, "bwd_dkdv": 2.0 * fwd_flops, "bwd_dq": 0.5 * fwd_flops}
     src = {"fwd": ("fwd_bf16.hip", "common.h"), "bwd_dkdv": ("bwd_bf16.hip", "common.h"),
            "bwd_dq": ("bwd_bf16.hip", "common.h")}
 
@@ -214,9 +218,9 @@ def main():
             ms = dom_ms  # measured inside the timed steps
         rec = {"ms": round(ms, 5)}
         if n in kernel_flops:
-            rec["tflops"] = round(kernel_flops[n] / (ms * 1e-3) / 1e12, 2)
+            rec["tflops_executed"] = round(kernel_flops[n] / (ms * 1e-3) / 1e12, 2)
+            rec["tflops_counted"] = round(kernel_flops_counted[n] / (ms * 1e-3) / 1e12, 2)
         kernels[n] = rec
-    kernels["fwd"]["tflops_counted"] = kernels["fwd"]["tflops"]
     bwd_ms = sum(kernels[n]["ms"] for n, _ in launches[1:])
     kernels["bwd_total"] = {"ms": round(bwd_ms, 5),
                             "tflops_counted": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)}
@@ -285,6 +289,20 @@ def timed(torch, np, fn, reps, warm=2):
     torch.cuda.synchronize()
     ts = [s.elapsed_time(e) for s, e in evs]
     return float(np.median(ts)), float(np.min(ts))
+
+
+def timed_batch(torch, fn, n):
+    """GPU time per call of n back-to-back calls between two events (the
+    queue stays full, so per-call event overhead is not part of it)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def graph_timed(torch, np, make_calls, reps=10):
@@ -485,9 +503,21 @@ def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
     w = inputs.doc_mask()
     q, k, v = to_dev(w["q"]), to_dev(w["k"]), to_dev(w["v"])
     doc = torch.from_numpy(w["doc"]).to(dev)
-    med_m, _ = timed(torch, np, lambda: b.block_mask_build(2, 8192, 8192, 128, 128, causal=True,
-                                                            doc_q=doc, doc_k=doc), 10)
     m = b.block_mask_build(2, 8192, 8192, 128, 128, causal=True, doc_q=doc, doc_k=doc)
+    # the build alone: the C call on a preallocated buffer
+    desc = b.attn_mask_desc()
+    desc.causal, desc.window_left, desc.window_right = 1, -1, -1
+    desc.doc_q = desc.doc_k = doc.data_ptr()
+    mout = b.attn_block_mask()
+    nbytes = lib.attn_block_mask_bytes(2, 8192, 8192, 128, 128)
+    mbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    build = Prepared(lib.block_mask_build, (ctypes.byref(desc), 2, 8192, 8192, 128, 128,
+                                            b._ptr(mbuf), nbytes, ctypes.byref(mout),
+                                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    med_m, _ = timed(torch, np, build, 10)
+    batch_m = timed_batch(torch, build, 50)
+    same = all(torch.equal(x, y) for x, y in zip(m.arrays().values(),
+                                                  b.BlockMask(mout, mbuf, doc, doc).arrays().values()))
     oo = torch.empty_like(q)
     ll = torch.empty((2, 16, 8192), dtype=torch.float32, device=dev)
     med, _ = timed(torch, np, lambda: b.attn_fwd(q, k, v, softmax_scale=w["scale"], block_mask=m,
@@ -505,7 +535,10 @@ def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
                                        b._tensor(oo), b._tensor(do), b._ptr(ll), b._tensor(gq),
                                        b._tensor(gk), b._tensor(gv), 1, b._ptr(wsb), wsb.numel(), stream))
     med_b, _ = timed(torch, np, bwd_call, 10)
-    ex["doc_mask_s8192_d64"] = {"block_mask_build_ms": round(med_m, 4), "fwd_ms": round(med, 4),
+    ex["doc_mask_s8192_d64"] = {"block_mask_build_ms": round(batch_m, 4),
+                                "block_mask_build_single_call_ms": round(med_m, 4),
+                                "block_mask_repeat_equal": same,
+                                "fwd_ms": round(med, 4),
                                 "tflops": round(fl / (med * 1e-3) / 1e12, 2),
                                 "frac_of_bf16_peak": round(fl / (med * 1e-3) / 1e12 /
                                                            PEAK_BF16_TFLOPS, 4),
@@ -514,27 +547,123 @@ def extra_workloads(b, lib, inputs, torch, np, dev, to_dev):
     return ex
 
 
-def cpu_baseline(w, step_flops):
-    """The fp64 oracle (as it stands) on one full fwd + bwd step of the same
-    workload, on this host's cores."""
-    sys.path.insert(0, ROOT)
-    import oracle
-    from exact_attention_10_amd import inputs
+def cpu_identity():
+    """Host cores this process may use, the CPU model and numpy's BLAS."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default
-        threads = len(os.sched_getaffinity(0))
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = "%s %s" % (i.get("internal_api"), i.get("version"))
+                break
+    except Exception:
+        pass
+    return cores, model, blas
+
+
+def cpu_baseline(w, step_flops):
+    """The fp64 oracle (as it stands) on this host's cores, per workload: a
+    thread pool over independent (batch, head-group[, row block]) units, one
+    BLAS thread per worker (numpy releases the GIL inside BLAS and ufuncs).
+    Every workload is run whole except the long-context one, which runs 8 of
+    its 32 query heads per modifier (scaled by 4)."""
+    import concurrent.futures
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import oracle
+    from exact_attention_10_amd import inputs
+    cores, model, blas = cpu_identity()
+    workers = max(1, min(cores, 16))
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:
+        limit = None
+
+    def run(units):
+        t0 = time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda f: f(), units))
+        return time.perf_counter() - t0
+
+    per = {}
+    # tiny dense forward, fp32 inputs: B=1 Hq=Hkv=2 S=128 D=64
+    t = inputs.tiny_dense()
+    f = {n: inputs.as_f64(t[n], t["dtype"]) for n in ("q", "k", "v")}
+    dt = run([lambda h=h: oracle.attention_fwd_rows(f["q"], f["k"], f["v"], 0, h, np.arange(128),
+                                                     scale=t["scale"]) for h in range(2)])
+    per["tiny_dense_fwd"] = {"seconds": round(dt, 4)}
+    # the headline workload, forward and backward (units: kv-head groups)
     q, k, v, do = (inputs.as_f64(w[n], "bf16") for n in ("q", "k", "v", "do"))
-    t0 = time.perf_counter()
-    oracle.attention_fwd(q, k, v, scale=w["scale"], causal=True)
-    oracle.attention_bwd(q, k, v, do, scale=w["scale"], causal=True)
-    dt = time.perf_counter() - t0
-    return {"value": round(step_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "one full fwd+bwd step of the B=1 Hq=32 Hkv=8 S=2048 D=128 causal "
-                      "workload, fp64 numpy (BLAS threads = cores)"}
+    G = q.shape[2] // k.shape[2]
+    grp = [(slice(G * g, G * g + G), slice(g, g + 1)) for g in range(k.shape[2])]
+    dt_f = run([lambda hs=hs, ks=ks: oracle.attention_fwd(q[:, :, hs], k[:, :, ks], v[:, :, ks],
+                                                           scale=w["scale"], causal=True)
+                for hs, ks in grp])
+    dt_b = run([lambda hs=hs, ks=ks: oracle.attention_bwd(q[:, :, hs], k[:, :, ks], v[:, :, ks],
+                                                           do[:, :, hs], scale=w["scale"], causal=True)
+                for hs, ks in grp])
+    fwd_flops = step_flops / 3.5
+    per["llama8b_fwd"] = {"seconds": round(dt_f, 3), "tflops": round(fwd_flops / dt_f / 1e12, 5)}
+    per["llama8b_bwd"] = {"seconds": round(dt_b, 3), "tflops": round(2.5 * fwd_flops / dt_b / 1e12, 5)}
+    # long-context local attention (8 of 32 heads, x4), ALiBi and softcap runs
+    ll = inputs.long_local()
+    q3, k3, v3 = (inputs.as_f64(ll[n], "bf16") for n in ("q", "k", "v"))
+    pairs3 = 4096 * 4097 // 2 + (16384 - 4096) * 4097
+    for name, kw in (("alibi", dict(alibi_slopes=ll["alibi_slopes"])), ("softcap50", dict(softcap=50.0))):
+        units = [lambda h=h, r0=r0: oracle.attention_fwd_rows(q3, k3, v3, 0, h, np.arange(r0, r0 + 2048),
+                                                               scale=ll["scale"], causal=True,
+                                                               window=(4096, 0), **kw)
+                 for h in range(0, 32, 4) for r0 in range(0, 16384, 2048)]
+        dt = 4.0 * run(units)
+        per["long_local_" + name + "_fwd"] = {"seconds": round(dt, 3),
+                                              "tflops": round(4.0 * 32 * 128 * pairs3 / dt / 1e12, 5),
+                                              "measured_heads": 8}
+    del q3, k3, v3
+    # packed-document mask forward (documents are independent: one unit per document)
+    dm = inputs.doc_mask()
+    q4, k4, v4 = (inputs.as_f64(dm[n], "bf16") for n in ("q", "k", "v"))
+    units = []
+    for bb in range(2):
+        s0 = 0
+        for n in dm["doc_lengths"][bb]:
+            sl = slice(s0, s0 + n)
+            units.append(lambda bb=bb, sl=sl: oracle.attention_fwd(q4[bb:bb + 1, sl], k4[bb:bb + 1, sl],
+                                                                   v4[bb:bb + 1, sl], scale=dm["scale"],
+                                                                   causal=True))
+            s0 += n
+    dt = run(units)
+    pairs4 = sum(n * (n + 1) // 2 for lb in dm["doc_lengths"] for n in lb)
+    per["doc_mask_fwd"] = {"seconds": round(dt, 3), "tflops": round(4.0 * 16 * 64 * pairs4 / dt / 1e12, 5)}
+    del q4, k4, v4
+    # MQA decode over the cache (one unit per sequence)
+    dc = inputs.decode_mqa()
+    q5, k5, v5 = (inputs.as_f64(dc[n], "bf16") for n in ("q", "k", "v"))
+    lens = dc["cache_seqlens"]
+    dt = run([lambda bb=bb: oracle.decode(q5[bb:bb + 1], k5[bb:bb + 1], v5[bb:bb + 1], lens[bb:bb + 1],
+                                          scale=dc["scale"]) for bb in range(len(lens))])
+    dec_bytes = int(lens.sum()) * 128 * 2 * 2 + 2 * 32 * 128 * 128 * 2 + 32 * 128 * 4
+    per["decode_mqa"] = {"seconds": round(dt, 4), "gbs": round(dec_bytes / dt / 1e9, 3)}
+    if limit is not None:
+        limit.unregister() if hasattr(limit, "unregister") else None
+    step_s = dt_f + dt_b
+    return {"value": round(step_flops / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle", "seconds": round(step_s, 3), "cpu_model": model,
+            "host_cores_available": cores, "blas": blas, "per_config": per,
+            "sample": "value: one full fwd+bwd step of the B=1 Hq=32 Hkv=8 S=2048 D=128 causal "
+                      "workload (fp64 numpy oracle, %d worker threads over kv-head groups, one BLAS "
+                      "thread each); per_config: every workload whole except the 16K window one "
+                      "(8 of 32 heads, scaled x4)" % workers}
 
 
 if __name__ == "__main__":
