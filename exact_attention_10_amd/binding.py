@@ -133,8 +133,11 @@ _lib.attn_decode_noalloc_max_bytes.restype = ctypes.c_size_t
 _lib.attn_decode_noalloc_max_bytes.argtypes = []
 _lib.attn_debug_set_spin_limit.restype = None
 _lib.attn_debug_set_spin_limit.argtypes = [ctypes.c_int32]
+_lib.attn_set_bwd_gqa_schedule.restype = None
+_lib.attn_set_bwd_gqa_schedule.argtypes = [ctypes.c_int32]
 
 EXPORTED = ["attn_status_string", "attn_last_error", "attn_debug_set_spin_limit",
+            "attn_set_bwd_gqa_schedule",
             "attn_fwd", "attn_fwd_tile_shape",
             "attn_fwd_workspace_size",
             "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_size", "attn_decode",
@@ -606,6 +609,13 @@ def set_spin_limit(limit):
     """Testing hook (attn_debug_set_spin_limit): bound of the in-kernel
     waits for later launches; a negative value restores the default."""
     _lib.attn_debug_set_spin_limit(int(limit))
+
+
+def set_bwd_gqa_schedule(mode):
+    """attn_set_bwd_gqa_schedule: schedule of the dK/dV pass for grouped-query
+    heads in later launches (0 automatic, 1 per-head partials and a group
+    sum, 2 the group's heads looped inside each workgroup)."""
+    _lib.attn_set_bwd_gqa_schedule(int(mode))
 
 
 def decode_workspace_size(q, k_cache, num_splits=0, softcap=0.0, causal=False):

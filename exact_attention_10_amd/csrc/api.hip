@@ -16,8 +16,16 @@
 namespace attn {
 namespace {
 std::atomic<int> g_spin_limit{kDefaultSpinLimit};
+std::atomic<int> g_bwd_gqa_mode{0};
 }
 int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+bool bwd_group_loop_choice(long kv_grid, int cus) {
+  switch (g_bwd_gqa_mode.load(std::memory_order_relaxed)) {
+    case 1: return false;
+    case 2: return true;
+    default: return kv_grid >= 2L * cus;
+  }
+}
 }  // namespace attn
 
 namespace {
@@ -170,6 +178,10 @@ const char* attn_last_error(void) { return g_err; }
 
 void attn_debug_set_spin_limit(int32_t limit) {
   attn::g_spin_limit.store(limit < 0 ? attn::kDefaultSpinLimit : limit, std::memory_order_relaxed);
+}
+
+void attn_set_bwd_gqa_schedule(int32_t mode) {
+  attn::g_bwd_gqa_mode.store(mode == 1 || mode == 2 ? mode : 0, std::memory_order_relaxed);
 }
 
 attn_status attn_fwd_tile_shape(const attn_params* p, int32_t dtype, int32_t* block_m,

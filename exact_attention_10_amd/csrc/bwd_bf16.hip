@@ -763,7 +763,11 @@ __device__ __forceinline__ void pair_side_b(const char* qt_lds, const char* dot_
   }
 }
 
-template <typename T, int D, int MOD>
+// GL (grouped-query heads looped in the workgroup): a workgroup owns 128 keys
+// of one (batch, kv head) and streams the query tiles of the G query heads of
+// its group one head after another into the same dK/dV accumulators, which it
+// writes rounded once; without GL it owns 128 keys of one query head.
+template <typename T, int D, int MOD, bool GL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int partial) {
   using C = KVPairCfg<D>;
   // Three tile buffers (distinct LDS objects: a copy is never taken to alias
@@ -791,14 +795,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   const int pair = wave & 3;
   const int lo_row = PairOff<D>::row_lane(lane), lo_tr = PairOff<D>::tr_lane(lane);
   const int g = lane >> 5, c = lane & 31;
-  const int per = a.Hq * a.B;
+  const int Gq = a.Hq / a.Hkv;
+  const int nh = GL ? a.Hkv : a.Hq;  // heads the grid enumerates
+  const int per = nh * a.B;
   const int kt = blockIdx.x / per;  // key tiles near the start see the most causal rows
   const int rem = blockIdx.x % per;
-  const int b = rem / a.Hq;
-  int h = rem % a.Hq;
-  if ((a.Hq & 7) == 0) h = (h & 7) * (a.Hq >> 3) + (h >> 3);
-  const int Gq = a.Hq / a.Hkv;
-  const int kvh = h / Gq;
+  const int b = rem / nh;
+  int hw = rem % nh;
+  if ((nh & 7) == 0) hw = (hw & 7) * (nh >> 3) + (hw >> 3);
+  const int kvh = GL ? hw : hw / Gq;
+  const int h = GL ? kvh * Gq : hw;  // the (first) query head
+  const int nhead = GL ? Gq : 1;
 
   const bf16_t* qp = static_cast<const bf16_t*>(a.q) + b * a.q_sb + h * a.q_sh;
   const bf16_t* dop = static_cast<const bf16_t*>(a.dout) + b * a.do_sb + h * a.do_sh;
@@ -822,9 +829,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
       xf[ds] = __builtin_bit_cast(typename T::vec8, x);
     }
   }
-  const BwdCtx cx = make_ctx(a, b, h, MOD & 1, MOD & 2);
+  const BwdCtx cx0 = make_ctx(a, b, h, MOD & 1, MOD & 2);
 
-  // Query tiles that meet the workgroup's keys (as in the kernel above).
+  // Query tiles that meet the workgroup's keys (as in the kernel above), per
+  // head; with GL the step stream runs through them once per head.
   const RowWindow win(a.Sq, a.Sk, a.mask.causal, a.mask.wl, a.mask.wr);
   constexpr bool sparse = (MOD & 4) != 0;
   int qt_begin = 0, ntiles = 0, n_full_blk = 0;
@@ -839,12 +847,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   } else {
     const int c0 = kt * C::BN, c1 = min(a.Sk, c0 + C::BN) - 1;
     int i_lo = 0, i_hi = a.Sq - 1;
-    if (win.R != kUnbounded) i_lo = max(i_lo, c0 - cx.delta_pos - win.R);
-    if (win.L != kUnbounded) i_hi = min(i_hi, c1 - cx.delta_pos + win.L);
+    if (win.R != kUnbounded) i_lo = max(i_lo, c0 - cx0.delta_pos - win.R);
+    if (win.L != kUnbounded) i_hi = min(i_hi, c1 - cx0.delta_pos + win.L);
     qt_begin = i_lo <= i_hi ? i_lo / C::BM : 0;
     ntiles = i_lo <= i_hi ? i_hi / C::BM + 1 - qt_begin : 0;
   }
+  const int ntq = ntiles;  // query tiles per head
+  ntiles *= nhead;
+  // Step t is query tile t % ntq of head h + t / ntq.
+  auto head_of = [&](int t) __attribute__((always_inline)) -> int { return GL ? t / ntq : 0; };
   auto qt_of = [&](int t) __attribute__((always_inline)) -> int {
+    if (GL) t -= ntq * (t / ntq);
     if (!sparse) return qt_begin + t;
     const int blk = t >> 1;
     return 2 * (blk < n_full_blk ? qi_full[blk] : qi_part[blk - n_full_blk]) + (t & 1);
@@ -852,6 +865,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   // Whether this pair's 32 keys meet query tile t, and whether a predicate is needed.
   auto tile_state = [&](int t, int qt, bool* masked) __attribute__((always_inline)) -> bool {
     if (sparse) {
+      if (GL) t -= ntq * (t / ntq);
       *masked = (t >> 1) >= n_full_blk;
       return true;
     }
@@ -872,19 +886,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   // and their P' is zero for wave B).
   const TileCopy<D, C::NW> qcopy(qp, a.q_ss, a.Sq, wave, lane);
   const TileCopy<D, C::NW> dcopy(dop, a.do_ss, a.Sq, wave, lane);
-  auto load_tile = [&](int qt, auto buf_tag) __attribute__((always_inline)) {
+  auto load_tile = [&](int t, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
+    const int qt = qt_of(t), x = head_of(t);
     char* qd = BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2);
     char* dd = BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2);
-    qcopy(reinterpret_cast<bf16_t*>(qd), qt * C::BM);
-    dcopy(reinterpret_cast<bf16_t*>(dd), qt * C::BM);
-    const int i = min(qt * C::BM + lane, a.Sq - 1);
+    qcopy(reinterpret_cast<bf16_t*>(qd), qt * C::BM, (int64_t)x * a.q_sh);
+    dcopy(reinterpret_cast<bf16_t*>(dd), qt * C::BM, (int64_t)x * a.do_sh);
+    const int i = min(qt * C::BM + lane, a.Sq - 1) + x * a.Sq;
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(lsep + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2)), 4, 0, 0);
     else if (wave == 1)
       __builtin_amdgcn_global_load_lds(dlp + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? lg0 : (BUF == 1 ? lg1 : lg2)), 4, 0, 0);
     else if (wave == 2 && has_doc)
-      __builtin_amdgcn_global_load_lds(docq + i, (__attribute__((address_space(3))) void*)(BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2)), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(docq + i - x * a.Sq, (__attribute__((address_space(3))) void*)(BUF == 0 ? lz0 : (BUF == 1 ? lz1 : lz2)), 4, 0, 0);
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
@@ -896,7 +911,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  if (ntiles > 0) load_tile(qt_of(0), B0{});
+  if (ntiles > 0) load_tile(0, B0{});
   wait_dma();
   __syncthreads();
 
@@ -910,11 +925,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
     constexpr bool kA = decltype(role_tag)::value;
     using NEXT = std::integral_constant<int, (BUF + 1) % 3>;
     constexpr int PREV = (BUF + 2) % 3;
-    if (t + 1 < ntiles) load_tile(qt_of(t + 1), NEXT{});
+    if (t + 1 < ntiles) load_tile(t + 1, NEXT{});
     if constexpr (kA) {
       if (t < ntiles) {
         const int qt = qt_of(t);
         bool masked;
+        // the ALiBi slope is the only per-head term of the score
+        const BwdCtx cx = (GL && (MOD & 1)) ? make_ctx(a, b, h + head_of(t), true, MOD & 2) : cx0;
         if (tile_state(t, qt, &masked))
           pair_side_a<T, D, MOD>(BUF == 0 ? lq0 : (BUF == 1 ? lq1 : lq2), BUF == 0 ? ld0 : (BUF == 1 ? ld1 : ld2),
                                  lo_row, lo_tr, BUF == 0 ? ll0 : (BUF == 1 ? ll1 : ll2), xf, acc, cx, qt * C::BM, my_key, masked,
@@ -1309,10 +1326,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int fold) {
 template <typename T, int D, int MOD>
 hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int partial = G > 1 ? 1 : 0;
   static_assert(KVPairCfg<D>::BN == KVCfg<D>::BN, "both dK/dV kernels take 128 keys per workgroup");
   const int nkt = (a.Sk + KVCfg<D>::BN - 1) / KVCfg<D>::BN;
   const bool atomic_dq = a.dq_acc != nullptr;
+  constexpr bool kPairOk = D == 128 || !(MOD & 4);
+  // Grouped-query heads: loop the G heads inside each dK/dV workgroup (no
+  // per-head partials and no group sum) when the kv-head grid alone has at
+  // least two workgroups per CU to balance; else one workgroup per query
+  // head writes an fp32 partial and the group-sum kernel adds them up.
+  const bool group_loop = kPairOk && !atomic_dq && G > 1 &&
+                          bwd_group_loop_choice((long)nkt * a.Hkv * a.B, device_cu_count());
+  const int partial = (G > 1 && !group_loop) ? 1 : 0;
   // Deterministic schedule: stage 0 is the dQ kernel, which also writes
   // Delta and lse2 for the dK/dV kernel (no separate Delta pass).
   const int nqt0 = (a.Sq + QCfg<D>::BM - 1) / QCfg<D>::BM;
@@ -1333,9 +1357,13 @@ hipError_t launch_mod(const BwdArgs& a, int stages, hipStream_t s) {
     // kernel reads the block lists with vector loads it must wait for.
     if (atomic_dq)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, true>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
-    else if constexpr (D == 128 || !(MOD & 4))
-      hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, MOD>), dim3(nkt * a.Hq * a.B), dim3(512), 0, s, a, partial);
-    else
+    else if constexpr (kPairOk) {
+      if (group_loop)
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, MOD, true>), dim3(nkt * a.Hkv * a.B), dim3(512), 0, s, a, 0);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(512), 0, s, a,
+                           partial);
+    } else
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MOD, false>), dim3(nkt * a.Hq * a.B), dim3(256), 0, s, a, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -183,12 +183,13 @@ struct TileCopy {
       : src(src_), ld(ld_), nrows(nrows_), wave(wave_), lane(lane_) {
     lane_off = ((int64_t)(wave_ * L::RG + lane_ % L::RG) * ld_ + (lane_ / L::RG) * 8) * 2;
   }
-  __device__ __forceinline__ void operator()(bf16_t* tile, int row0) const {
+  // elem_off: elements added to the source (another head of the same layout)
+  __device__ __forceinline__ void operator()(bf16_t* tile, int row0, int64_t elem_off = 0) const {
     if (row0 + 64 > nrows) {
-      tile_dma<D, NW>(tile, src, ld, row0, nrows, wave, lane);
+      tile_dma<D, NW>(tile, src + elem_off, ld, row0, nrows, wave, lane);
       return;
     }
-    const char* base = reinterpret_cast<const char*>(src) + (int64_t)row0 * ld * 2;
+    const char* base = reinterpret_cast<const char*>(src + elem_off) + (int64_t)row0 * ld * 2;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const char* gp = base + (int64_t)u * NW * L::RG * ld * 2 + lane_off;

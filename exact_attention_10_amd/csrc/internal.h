@@ -52,6 +52,11 @@ struct FwdArgs {
 constexpr int kDefaultSpinLimit = 1 << 22;
 int spin_limit();
 
+// Whether the dK/dV kernel loops the grouped-query heads of a kv head inside
+// one workgroup (kv_grid: its workgroups then) rather than writing per-head
+// partials; attn_set_bwd_gqa_schedule can force either.
+bool bwd_group_loop_choice(long kv_grid, int cus);
+
 // bf16 MFMA forward.  Tiles of 128 or 256 query rows x 64 keys (block-sparse
 // masks use 128-row tiles).
 constexpr int kFwdBM = 128;

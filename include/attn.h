@@ -165,6 +165,21 @@ const char* attn_last_error(void);
  * process-wide; never fails. */
 void attn_debug_set_spin_limit(int32_t limit);
 
+/* Schedule of the dK/dV pass for grouped-query heads (Hq > Hkv), for
+ * launches enqueued after the call ([HF]: K and V are shared by the
+ * G = Hq / Hkv query heads of a group and never repeated, so dK and dV are
+ * sums over the group).
+ *   0 (default) automatic: mode 2 when the (batch, kv head, 128-key block)
+ *     grid has at least two workgroups per compute unit, else mode 1;
+ *   1 one workgroup per query head and 128-key block, each writing fp32
+ *     partial sums to the workspace, then a kernel that adds the G partials
+ *     of each kv head in head order;
+ *   2 one workgroup per kv head and 128-key block, looping over the G query
+ *     heads into the same accumulators (no partials, no group sum).
+ * Both are deterministic; they differ only in rounding order.  Any other
+ * value selects 0.  Host only; process-wide; never fails. */
+void attn_set_bwd_gqa_schedule(int32_t mode);
+
 /* ---------------------------------------------------------------------
  * Forward ([TA] "Tiling the Computation", "2. Online Softmax",
  * "3. Weighted Sum of Values"; [FA] flash_attn_func; [FX4] score and mask

@@ -60,6 +60,30 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
 def test_bwd_parity(b, case):
+    _bwd_case(b, case)
+
+
+@pytest.fixture
+def gqa_schedule(b):
+    """Sets attn_set_bwd_gqa_schedule for one test and restores automatic."""
+    yield b.set_bwd_gqa_schedule
+    b.set_bwd_gqa_schedule(0)
+
+
+GQA_CASES = [c for c in CASES if c[3] > c[4]]
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("case", GQA_CASES, ids=[str(i) for i in range(len(GQA_CASES))])
+def test_bwd_gqa_schedules(b, gqa_schedule, case, mode):
+    """Both dK/dV schedules for grouped-query heads (per-head partials plus a
+    group sum; the group's heads looped inside each workgroup) against the
+    oracle, whichever the automatic choice would take."""
+    gqa_schedule(mode)
+    _bwd_case(b, case)
+
+
+def _bwd_case(b, case):
     B, Sq, Sk, Hq, Hkv, D, opt = case
     w = inputs.random_case(300 + Sq + Sk + D, B, Sq, Sk, Hq, Hkv, D, dtype="bf16", grad=True)
     kw = dict(softmax_scale=opt.get("scale", 0.11 if D == 128 else 0.15),
@@ -91,6 +115,23 @@ def test_bwd_llama8b_full(b):
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+def test_bwd_llama8b_group_loop(b, gqa_schedule):
+    """The same workload with the G = 4 query heads of each kv head looped
+    inside the dK/dV workgroups: every dK/dV element against the oracle, dQ
+    unchanged bit for bit, and a second run bitwise identical."""
+    w = inputs.llama8b_train()
+    kw = dict(softmax_scale=w["scale"], causal=True)
+    dq1, _, _ = run_bwd(b, w, **kw)
+    gqa_schedule(2)
+    dq, dk, dv = run_bwd(b, w, **kw)
+    assert torch.equal(dq, dq1)
+    _, rk, rv = oracle_grads(w, kw)
+    check_o(to_f64(dk), rk, GRAD_ATOL, "dK")
+    check_o(to_f64(dv), rv, GRAD_ATOL, "dV")
+    dq2, dk2, dv2 = run_bwd(b, w, **kw)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
 # ---------------------------------------------------------------------------
 # Block-sparse backward ([GYM] create_block_mask; [FX4] block sparsity): the
 # dK/dV kernel walks each key block's query-block lists, the dQ kernel each
@@ -108,6 +149,17 @@ SPARSE_CASES = [
 
 @pytest.mark.parametrize("case", SPARSE_CASES, ids=[str(i) for i in range(len(SPARSE_CASES))])
 def test_bwd_block_sparse(b, case):
+    _sparse_case(b, case)
+
+
+def test_bwd_block_sparse_group_loop(b, gqa_schedule):
+    """A grouped-query block-sparse case with the heads looped in the dK/dV
+    workgroups (the query-block lists are walked once per head)."""
+    gqa_schedule(2)
+    _sparse_case(b, (2, 300, 8, 2, 128, 128, True, (-1, -1), (20, 90), {"alibi": True}))
+
+
+def _sparse_case(b, case):
     B, S, Hq, Hkv, D, bn, causal, window, doc_range, opt = case
     w = inputs.random_case(700 + S + D, B, S, S, Hq, Hkv, D, dtype="bf16", grad=True,
                            doc_len_range=doc_range)
@@ -155,10 +207,14 @@ def test_bwd_doc_mask_s8192(b):
         assert s0 == 8192
 
 
-def test_bwd_alibi_per_batch_slopes(b):
+@pytest.mark.parametrize("mode", [1, 2])
+def test_bwd_alibi_per_batch_slopes(b, gqa_schedule, mode):
     """Backward with ALiBi slopes of shape (batch, nheads) ("FlashAttention:
     Fast and Memory-Efficient Exact Attention", "Examples"): every gradient
-    element against the oracle with the same per-batch table."""
+    element against the oracle with the same per-batch table, under both
+    grouped-query dK/dV schedules (the slope is the per-head term the
+    in-workgroup head loop must switch)."""
+    gqa_schedule(mode)
     B, S, Hq, Hkv, D = 3, 300, 4, 2, 128
     w = inputs.random_case(71, B, S, S, Hq, Hkv, D, dtype="bf16", grad=True)
     slopes = np.random.default_rng(72).uniform(0.05, 1.0, (B, Hq)).astype(np.float32)
