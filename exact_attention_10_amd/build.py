@@ -24,8 +24,12 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-file flags (none at present; kept so a translation unit can get its own).
-FILE_FLAGS = {}
+# Per-file flags.  The forward's row maxima are taken on matrix-core results
+# and masked -inf values, never on NaN operands: without IEEE NaN handling
+# (hardware IEEE mode off, no NaN operands assumed) fmaxf is one v_max_f32
+# instead of two NaN-quieting v_max_f32 plus the max.  The kernel writes its
+# NaN poison as integer bit patterns.
+FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src, verbose):

@@ -53,11 +53,13 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 struct Bf16T {
   using vec8 = bf16x8;
   using elem = __bf16;
+  static constexpr uint32_t kNan2 = 0x7FC07FC0u;  // two quiet NaNs
   __device__ static float to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
 };
 struct F16T {
   using vec8 = f16x8;
   using elem = _Float16;
+  static constexpr uint32_t kNan2 = 0x7E007E00u;  // two quiet NaNs
   __device__ static float to_f32(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
 };
 template <typename T>

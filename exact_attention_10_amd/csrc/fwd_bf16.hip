@@ -523,11 +523,12 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
     m_run = M;
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2.  Poisoned rows get
+  // NaN bit patterns written as integers (this file is compiled assuming no
+  // NaN operands, so no arithmetic may produce them).
   const float l_tot = l_run + wave_xor32(l_run);
   if (q_ok) {
-    float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (broken) inv = __builtin_nanf("");
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     bf16_t* op = static_cast<bf16_t*>(a.o) + b * a.o_sb + (int64_t)my_q * a.o_ss + h * a.o_sh;
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db) {
@@ -537,12 +538,15 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
         uint2 packed;
         packed.x = f32_to_elem<T>(oacc[db][4 * rr + 0] * inv) | (uint32_t)f32_to_elem<T>(oacc[db][4 * rr + 1] * inv) << 16;
         packed.y = f32_to_elem<T>(oacc[db][4 * rr + 2] * inv) | (uint32_t)f32_to_elem<T>(oacc[db][4 * rr + 3] * inv) << 16;
+        if (broken) packed = make_uint2(T::kNan2, T::kNan2);
         *reinterpret_cast<uint2*>(op + d0) = packed;
       }
     }
-    if (g == 0)
-      a.lse[((int64_t)b * a.Hq + h) * a.Sq + my_q] =
-          broken ? __builtin_nanf("") : (l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf);
+    if (g == 0) {
+      const float lse = l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      reinterpret_cast<uint32_t*>(a.lse)[((int64_t)b * a.Hq + h) * a.Sq + my_q] =
+          broken ? 0x7FC00000u : __float_as_uint(lse);
+    }
   }
 }
 
