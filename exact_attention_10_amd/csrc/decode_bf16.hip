@@ -59,7 +59,7 @@ struct DecCfg {
   static constexpr int GROUPS = BN / L::RG;           // 1 KB copy groups per 32-row tile
   static constexpr int TB = GROUPS * L::GS;           // bytes of one 32-row tile image
   static constexpr int SB = 2 * TB;                   // ring item: K then V, or 2 query blocks
-  static constexpr int NS = D == 128 ? 5 : 9;         // ring depth
+  static constexpr int NS = D == 128 ? 7 : 15;        // ring depth
   static constexpr int DEPTH = NS - 1;                // items a producer keeps unpublished in flight
   static constexpr int PER = 2 * GROUPS / NWP;        // copies per producer lane per ring item
   static constexpr int WIN = 512;                     // cache lengths kept in LDS
@@ -69,7 +69,10 @@ struct DecCfg {
   static constexpr int SEG = 4;
   static constexpr int DSTEPS = D / 16;
   static constexpr int DBLK = D / 32;
-  static constexpr int MSLOT = 64 * (16 * DBLK + 2);  // floats of one wave's softmax state
+  // One wave's softmax state handed over at a segment end: the unnormalised
+  // output rounded to bf16 (16 * DBLK values per lane, lane-major pairs)
+  // and the fp32 row maximum and sum.
+  static constexpr int MSLOT = 64 * (16 * DBLK * 2 + 8);  // bytes
 };
 
 // Bounded spin on an LDS flag: the waves of a workgroup hand items over with
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   using C = DecCfg<D>;
   using L = typename C::L;
   __shared__ __attribute__((aligned(16))) char ring[C::NS * C::SB];
-  __shared__ __attribute__((aligned(16))) float mrg[4 * C::MSLOT];
+  __shared__ __attribute__((aligned(16))) char mrg[4 * C::MSLOT];
   __shared__ int win_len[C::WIN];
   __shared__ long long red[C::NWT];
   __shared__ int landed[C::NWP];       // items whose copies by producer p have landed
@@ -570,18 +573,24 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     const bool active = hb * 32 < cc.rows;
     const int64_t j = (int64_t)cc.b * jpb + cc.jb;
     const int64_t slot = w_id + j;
-    float* ms = mrg + hb * C::MSLOT;
+    char* ms = mrg + hb * C::MSLOT;
+    uint2* ms_o = reinterpret_cast<uint2*>(ms);                       // [DBLK * 4][64] pairs of pairs
+    float* ms_ml = reinterpret_cast<float*>(ms + 64 * 16 * C::DBLK * 2);  // m [64], l [64]
     if (par == 1) {
       note(spin_until_ge(&mrg_read[hb], seg, a.spin_limit));  // the previous segment's state has been taken
       if (active) {
+        // bf16 is enough here: the merged partial is itself stored rounded
+        // to the input type, and the state's relative rounding (2^-9) adds
+        // to that once
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
-            *reinterpret_cast<float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4) =
-                make_float4(oacc[db][4 * rr], oacc[db][4 * rr + 1], oacc[db][4 * rr + 2], oacc[db][4 * rr + 3]);
-        ms[16 * C::DBLK * 64 + lane] = m_run;
-        ms[16 * C::DBLK * 64 + 64 + lane] = l_run;
+            ms_o[(db * 4 + rr) * 64 + lane] =
+                make_uint2(f32_to_elem<Bf16T>(oacc[db][4 * rr]) | (uint32_t)f32_to_elem<Bf16T>(oacc[db][4 * rr + 1]) << 16,
+                           f32_to_elem<Bf16T>(oacc[db][4 * rr + 2]) | (uint32_t)f32_to_elem<Bf16T>(oacc[db][4 * rr + 3]) << 16);
+        ms_ml[lane] = m_run;
+        ms_ml[64 + lane] = l_run;
       }
       if (lane == 0) publish(&mrg_written[hb], seg + 1);
       return;
@@ -589,8 +598,8 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     note(spin_until_ge(&mrg_written[hb], seg + 1, a.spin_limit));
     const bool poison = broken || __hip_atomic_load(&ring_broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (active) {
-      const float mo = ms[16 * C::DBLK * 64 + lane];
-      const float lo1 = ms[16 * C::DBLK * 64 + 64 + lane];
+      const float mo = ms_ml[lane];
+      const float lo1 = ms_ml[64 + lane];
       const float M = fmaxf(m_run, mo);
       const float a0 = m_run == kNegInf ? 0.0f : fast_exp2(m_run - M);
       const float a1 = mo == kNegInf ? 0.0f : fast_exp2(mo - M);
@@ -603,7 +612,9 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float4 x = *reinterpret_cast<const float4*>(ms + ((db * 4 + rr) * 64 + lane) * 4);
+          const uint2 xp = ms_o[(db * 4 + rr) * 64 + lane];
+          const float4 x = make_float4(Bf16T::to_f32(xp.x & 0xffffu), Bf16T::to_f32(xp.x >> 16),
+                                       Bf16T::to_f32(xp.y & 0xffffu), Bf16T::to_f32(xp.y >> 16));
           const float o0 = oacc[db][4 * rr] * s0 + x.x * s1, o1 = oacc[db][4 * rr + 1] * s0 + x.y * s1;
           const float o2 = oacc[db][4 * rr + 2] * s0 + x.z * s1, o3 = oacc[db][4 * rr + 3] * s0 + x.w * s1;
           const uint2 w2 = make_uint2(f32_to_elem<T>(o0) | (uint32_t)f32_to_elem<T>(o1) << 16,

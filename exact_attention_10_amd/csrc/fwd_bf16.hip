@@ -524,8 +524,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2.  Poisoned rows get
-  // NaN bit patterns written as integers (this file is compiled assuming no
-  // NaN operands, so no arithmetic may produce them).
+  // NaN bit patterns written as integers.
   const float l_tot = l_run + wave_xor32(l_run);
   if (q_ok) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
