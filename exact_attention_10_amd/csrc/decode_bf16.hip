@@ -62,7 +62,6 @@ struct DecCfg {
   static constexpr int NS = D == 128 ? 7 : 15;        // ring depth
   static constexpr int DEPTH = NS - 1;                // items a producer keeps unpublished in flight
   static constexpr int PER = 2 * GROUPS / NWP;        // copies per producer lane per ring item
-  static constexpr int WIN = 512;                     // cache lengths kept in LDS
   // Schedule weight of a job segment (query load, state merge, partial
   // write) in 32-key steps: each job counts SEG extra units in the split, so
   // a workgroup that starts a job takes that many fewer key steps.
@@ -150,40 +149,27 @@ __device__ __forceinline__ void wait_items(int k) {
 #undef ATTN_WAIT_CASE
 }
 
-// Workgroup-wide sum and exclusive prefix of one value per thread.
-template <int NWAVE>
-__device__ __forceinline__ long long block_sum(long long v, long long* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Wave-wide sum and inclusive prefix sum of one value per lane.
+__device__ __forceinline__ long long wave_sum64(long long v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  if (lane == 0) sh[wave] = v;
-  __syncthreads();
-  long long t = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) t += sh[w];
-  __syncthreads();
-  return t;
+  return v;
 }
-template <int NWAVE>
-__device__ __forceinline__ long long block_excl_scan(long long v, long long* sh, long long* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  long long x = v;
+// A wave-uniform 64-bit value moved to scalar registers (the compiler cannot
+// see that a cross-lane reduction gives every lane the same value).
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ long long wave_incl_scan64(long long x, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const long long y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  long long off = 0, t = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    off += w < wave ? sh[w] : 0;
-    t += sh[w];
-  }
-  *total = t;
-  __syncthreads();
-  return off + x - v;
+  return x;
 }
 
 // Position in one workgroup's sequence of ring items: job (b, jb) with
@@ -201,13 +187,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   using L = typename C::L;
   __shared__ __attribute__((aligned(16))) char ring[C::NS * C::SB];
   __shared__ __attribute__((aligned(16))) char mrg[4 * C::MSLOT];
-  __shared__ int win_len[C::WIN];
-  __shared__ long long red[C::NWT];
   __shared__ int landed[C::NWP];       // items whose copies by producer p have landed
   __shared__ int consumed[C::NWC];     // items consumer wave w is done with
   __shared__ int mrg_written[4], mrg_read[4];  // merge handshakes per head block
   __shared__ int ring_broken;          // some wave's wait expired (its data may be stale)
-  __shared__ long long sh_b0, sh_off0;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -220,61 +203,52 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   const int P = gridDim.x;
   const int w_id = blockIdx.x;
 
-  // ---- this workgroup's step range [lo, hi) ----
-  long long S, lo, hi;
-  if (a.B <= C::NT) {  // one pass: every thread keeps its sequence's length
-    const int Lt = tid < a.B ? seq_len(a, tid) : 0;
-    const int n = (Lt + C::BN - 1) / C::BN;
-    const long long units = n > 0 ? (long long)(n + C::SEG) * jpb : 0;
-    const long long pre = block_excl_scan<C::NWT>(units, red, &S);
-    const int Pe = S < P ? (int)S : P;
-    if (w_id >= Pe) return;
-    lo = (long long)w_id * S / Pe;
-    hi = (long long)(w_id + 1) * S / Pe;
-    if (n > 0 && pre <= lo && lo < pre + units) {
-      sh_b0 = tid;
-      sh_off0 = lo - pre;
-    }
-    __syncthreads();
-    const int b0 = (int)sh_b0;
-    if (tid >= b0 && tid - b0 < C::WIN) win_len[tid - b0] = Lt;
-    for (int i = tid + (a.B - b0); i < C::WIN; i += C::NT) win_len[i] = 0;
-  } else {
-    S = 0;
-    for (int base = 0; base < a.B; base += C::NT) {
-      const int b = base + tid;
-      const int n = b < a.B ? (seq_len(a, b) + C::BN - 1) / C::BN : 0;
-      S += block_sum<C::NWT>(n > 0 ? n + C::SEG : 0, red);
-    }
-    S *= jpb;
-    const int Pe = S < P ? (int)S : P;
-    if (w_id >= Pe) return;
-    lo = (long long)w_id * S / Pe;
-    hi = (long long)(w_id + 1) * S / Pe;
-    long long carry = 0;
-    for (int base = 0; base < a.B; base += C::NT) {
-      const int b = base + tid;
-      const int n = b < a.B ? (seq_len(a, b) + C::BN - 1) / C::BN : 0;
-      const long long units = n > 0 ? (long long)(n + C::SEG) * jpb : 0;
-      long long tot;
-      const long long pre = carry + block_excl_scan<C::NWT>(units, red, &tot);
-      if (n > 0 && pre <= lo && lo < pre + units) {
-        sh_b0 = b;
-        sh_off0 = lo - pre;
-      }
-      carry += tot;
-    }
-    __syncthreads();
-    const int b0 = (int)sh_b0;
-    for (int i = tid; i < C::WIN; i += C::NT)
-      win_len[i] = b0 + i < a.B ? seq_len(a, b0 + i) : 0;
-  }
+  // ---- counters first (zero before anyone publishes), then every wave
+  // finds this workgroup's step range [lo, hi) and first job by itself:
+  // wave-wide sums and prefix sums over the sequences, 64 at a time, so no
+  // workgroup barrier stands between the cache lengths and the first copies.
   if (tid < C::NWP) landed[tid] = 0;
   if (tid < C::NWC) consumed[tid] = 0;
   if (tid < 4) mrg_written[tid] = mrg_read[tid] = 0;
   if (tid == 0) ring_broken = 0;
   __syncthreads();
-  const int b0 = (int)sh_b0;
+  // Lengths of sequences c*64 .. c*64 + 63 for chunk c, one per lane; chunk
+  // 0 is loaded once and kept (a workgroup's range rarely goes past it).
+  auto lens_chunk = [&](int c) -> int { return c * 64 + lane < a.B ? seq_len(a, c * 64 + lane) : 0; };
+  const int len0 = lens_chunk(0);
+  auto units_of = [&](int L) -> long long {
+    const int n = (L + C::BN - 1) / C::BN;
+    return n > 0 ? (long long)(n + C::SEG) * jpb : 0;
+  };
+  long long S = wave_sum64(units_of(len0));
+  for (int c = 1; c * 64 < a.B; ++c) S += wave_sum64(units_of(lens_chunk(c)));
+  S = uniform64(S);
+  const int Pe = S < P ? (int)S : P;
+  if (w_id >= Pe) return;  // the same for every wave of the workgroup
+  const long long lo = (long long)w_id * S / Pe;
+  const long long hi = (long long)(w_id + 1) * S / Pe;
+  // The sequence whose units contain lo, and the offset of lo inside them.
+  int b0 = 0;
+  long long off0 = 0;
+  {
+    long long carry = 0;
+    for (int c = 0; c * 64 < a.B; ++c) {
+      const long long u = units_of(c == 0 ? len0 : lens_chunk(c));
+      const long long incl = carry + wave_incl_scan64(u, lane);
+      const uint64_t hit = __ballot(u > 0 && incl - u <= lo && lo < incl);
+      if (hit != 0) {
+        const int src = __builtin_ctzll(hit);
+        b0 = c * 64 + src;
+        const long long excl = __shfl(incl, src, 64) - __shfl(u, src, 64);
+        // (wave-uniform; readfirstlane tells the compiler so, keeping the
+        // cursor in scalar registers)
+        off0 = __builtin_amdgcn_readfirstlane(static_cast<int>(lo - excl));
+        break;
+      }
+      carry = __shfl(incl, 63, 64);
+    }
+  }
+  b0 = __builtin_amdgcn_readfirstlane(b0);
   // A wait of this wave that expired: its data may be stale, so the rows it
   // contributes to are written as NaN and the status word records it.
   bool broken = false;
@@ -301,7 +275,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   auto consumed_min = [&]() { return counters_min(consumed, std::integral_constant<int, C::NWC>{}); };
 
   auto len_of = [&](int b) -> int {
-    return b - b0 < C::WIN ? win_len[b - b0] : seq_len(a, b);
+    return __builtin_amdgcn_readfirstlane(b < 64 ? __shfl(len0, b, 64) : seq_len(a, b));
   };
   auto set_job = [&](Cursor& cu) {
     cu.g_kv = cu.jb / a.nhg;
@@ -316,7 +290,7 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     // The range starts in job jb at unit pos; a job's first SEG units are
     // its segment weight, so a start inside them means the job's first step
     // (and the rest of those units come out of the range).
-    const int off = (int)sh_off0;
+    const int off = (int)off0;
     const int per_job = cu.n + C::SEG;
     cu.jb = off / per_job;
     const int pos = off - cu.jb * per_job;
@@ -720,6 +694,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       if (lane == 0) publish(&consumed[wave], i + gsz);
     } else {
       const bool mine = par < gsz && hb * 32 < cc.rows;
+      // A parity-1 wave never reads item i of the group, so it is done with
+      // every item before i + 1 already; saying so at once lets the slot of
+      // item i be refilled as soon as the parity-0 waves are past it.
+      if (par == 1 && lane == 0) publish(&consumed[wave], i + 1);
       if (mine) {
         wait_landed(i + par + 1);
         kv_group(One{}, i + par, cc.step + par, cc.Lb);
