@@ -335,6 +335,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 
   int pg_b = -1, pg_blk = -1, pg_page = 0;  // last page lookup (producers)
   int cb_b = -1, cb_row = 0;                // last batch-row lookup (producers)
+  // Byte offset of copy u of this lane from its matrix's first row of a full
+  // K/V item (set by the producer waves before their loop, so that a full
+  // item costs one 64-bit add per copy).
+  int64_t poff[C::PER];
   auto issue = [&](const Cursor& pc, int slot) {
     // (Lane constants are recomputed here so that they do not occupy
     // registers in the consumer waves.)
@@ -375,14 +379,10 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
       const char* kb = static_cast<const char*>(a.k) + (koff + (int64_t)pc.g_kv * a.k_sh) * 2;
       const char* vb = static_cast<const char*>(a.v) + (voff + (int64_t)pc.g_kv * a.v_sh) * 2;
       if (row0 + C::BN <= pc.Lb) {
-        const int64_t koff = ((int64_t)lrow * a.k_ss + cp_chunk * 8) * 2;  // bytes, from a group's first row
-        const int64_t voff = ((int64_t)lrow * a.v_ss + cp_chunk * 8) * 2;
 #pragma unroll
         for (int u = 0; u < C::PER; ++u) {
           const int cpy = pw + C::NWP * u, mat = cpy / C::GROUPS, grp = cpy % C::GROUPS;
-          const char* src = mat ? vb + (int64_t)grp * L::RG * a.v_ss * 2 + voff
-                                : kb + (int64_t)grp * L::RG * a.k_ss * 2 + koff;
-          dma16(src, lds_addr(item + mat * C::TB + grp * L::GS));
+          dma16((mat ? vb : kb) + poff[u], lds_addr(item + mat * C::TB + grp * L::GS));
         }
       } else {  // the job's last step: rows past the cache length repeat the last one
 #pragma unroll
@@ -614,6 +614,14 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     // The producer shares its SIMD with consumer waves; a higher issue
     // priority keeps its copies flowing while they compute.
     __builtin_amdgcn_s_setprio(3);
+    {
+      const int lrow = lane % L::RG, cp_chunk = lane / L::RG;
+#pragma unroll
+      for (int u = 0; u < C::PER; ++u) {
+        const int cpy = pw + C::NWP * u, mat = cpy / C::GROUPS, grp = cpy % C::GROUPS;
+        poff[u] = ((int64_t)(grp * L::RG + lrow) * (mat ? a.v_ss : a.k_ss) + cp_chunk * 8) * 2;
+      }
+    }
     Cursor pc = cc;
     int issued = 0, published = 0;
     auto publish_all = [&]() {
