@@ -32,7 +32,7 @@
 // at the end of the job's segment).  The query heads play the role of query
 // rows of the forward kernel: S^T = K Q^T on the 32x32x16 matrix core.  K/V
 // tiles stream through an NS-deep LDS ring filled by direct global->LDS copies
-// that 2 producer waves issue and wait for, so the consumers never stall on
+// that 4 producer waves issue and wait for, so the consumers never stall on
 // the memory pipeline; each query block is itself a ring item, so the ring
 // never drains at a job change.  The hand-over uses LDS counters, not
 // barriers: producers and consumers each run at their own pace.
@@ -51,7 +51,7 @@ template <int D>
 struct DecCfg {
   static constexpr int ROWS = kDecodeRows;            // query heads per job
   static constexpr int NWC = 8;                       // consumers: 4 head blocks x 2 step parities
-  static constexpr int NWP = 2;                       // producer waves (copies only)
+  static constexpr int NWP = 4;                       // producer waves (copies only)
   static constexpr int NWT = NWC + NWP;
   static constexpr int NT = 64 * NWT;
   static constexpr int BN = 32;                       // keys per ring item
