@@ -158,13 +158,31 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
       }
   }
 
-  // Row maximum: tree over this lane's 32 values, then lane l ^ 32.
-  float m4[4];
+  // Row maximum over this lane's 32 values, then lane l ^ 32.  The first
+  // read of the accumulators is a compiled fmaxf, which carries the wait
+  // states after the MFMAs that wrote them; every three-input max in
+  // assembly after it depends on its result, so none is placed before it.
+  // (Compiled fmaxf in IEEE mode also quiets every operand first: 18
+  // instructions here against about 47.)
+  float v[32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    m4[i] = fmaxf(fmaxf(fmaxf(sacc[0][i], sacc[0][i + 4]), fmaxf(sacc[0][i + 8], sacc[0][i + 12])),
-                  fmaxf(fmaxf(sacc[1][i], sacc[1][i + 4]), fmaxf(sacc[1][i + 8], sacc[1][i + 12])));
-  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  for (int r = 0; r < 16; ++r) {
+    v[r] = sacc[0][r];
+    v[16 + r] = sacc[1][r];
+  }
+  float mc[4];
+  mc[0] = fmaxf(v[0], v[16]);
+  mc[1] = max3_nc(mc[0], v[1], v[2]);
+  mc[2] = max3_nc(mc[0], v[3], v[4]);
+  mc[3] = max3_nc(mc[0], v[5], v[6]);
+  // the other 24 values (7..15, 17..31) in pairs over the four chains
+#pragma unroll
+  for (int j = 0; j < 12; ++j) {
+    const int i0 = 7 + 2 * j < 16 ? 7 + 2 * j : 8 + 2 * j;   // 7, 9, 11, 13, 15, 17, ...
+    const int i1 = 7 + 2 * j + 1 < 16 ? 7 + 2 * j + 1 : 8 + 2 * j + 1;
+    mc[j & 3] = max3_nc(mc[j & 3], v[i0], v[i1]);
+  }
+  float mx = max_nc(max3_nc(mc[0], mc[1], mc[2]), mc[3]);
   mx = fmaxf(mx, wave_xor32(mx));
   const float mx2 = kScaled ? mx : mx * cx.scale_log2;  // -inf stays -inf
   if (__any(mx2 > m_run + kRescaleThreshold)) {
