@@ -741,7 +741,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int jr = hg * ROWS + r;  // row = query t * G + head
   const int t = jr / G;
   const int h = g_kv * G + (jr - t * G);
+  // The job's first and last workgroup are loaded beside its length, not
+  // after it: two dependent round trips become one.  (For an empty sequence
+  // they were never written and are not used.)
+  const int w0 = a.job_seg[2 * j], w1 = a.job_seg[2 * j + 1];
   const int Lb = seq_len(a, b);
+  asm volatile("" :: "v"(w0), "v"(w1), "v"(Lb));
   if (blockIdx.y == 0 && threadIdx.x == 0) {
     const int raw = a.seqlens[b];
     if (raw < 0 || raw > a.Smax - a.len_add) status_or(a.status, kDecodeStatusLength);
@@ -750,7 +755,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   float m = kNegInf, tot = 0.0f;
   bool poisoned = false;  // a partial was written as NaN (an expired wait)
   if (Lb > 0) {
-    const int w0 = a.job_seg[2 * j], w1 = a.job_seg[2 * j + 1];
     const float* pl = a.part_lse + ((int64_t)w0 + j) * ROWS + r;
     const uint16_t* po = a.part_o + (((int64_t)w0 + j) * ROWS + r) * D + 4 * d4;
     const int ns = w1 - w0 + 1;
