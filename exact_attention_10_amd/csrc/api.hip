@@ -480,6 +480,7 @@ static attn_status decode_impl(const attn_params* p, attn_tensor q, attn_tensor 
     strides3(kv->v_new, &a.vn_sb, &a.vn_ss, &a.vn_sh);
   }
   a.parts = attn::decode_parts(num_splits);
+  a.rows_job = attn::decode_job_rows(p->Hq, p->Hkv, p->Sq);
   a.nhg = attn::decode_head_groups(p->Hq, p->Hkv, p->Sq);
   const attn::DecodeWorkspace wl = attn::decode_workspace(p->B, p->Hq, p->Hkv, p->Sq, p->D, a.parts);
   char* wsb = static_cast<char*>(workspace);

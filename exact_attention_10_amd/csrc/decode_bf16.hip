@@ -47,10 +47,11 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-template <int D>
+template <int D, bool W = false>
 struct DecCfg {
-  static constexpr int ROWS = kDecodeRows;            // query heads per job
-  static constexpr int NWC = 8;                       // consumers: 4 head blocks x 2 step parities
+  // rows (query, head) per job; W: wide jobs, one 32-row block per consumer
+  static constexpr int ROWS = W ? kDecodeRowsWide : kDecodeRows;
+  static constexpr int NWC = 8;                       // consumers: 4 head blocks x 2 step parities, or 8 blocks (W)
   static constexpr int NWP = 4;                       // producer waves (copies only)
   static constexpr int NWT = NWC + NWP;
   static constexpr int NT = 64 * NWT;
@@ -172,8 +173,8 @@ __device__ __forceinline__ long long wave_incl_scan64(long long x, int lane) {
   return x;
 }
 
-// Position in one workgroup's sequence of ring items: job (b, jb) with
-// jb = kv head * nhg + head group, key step `step` of that job; `phase` < nq
+// Position in one workgroup's sequence of ring items: job (hg, b, jb) with
+// head group hg, sequence b and kv head jb, key step `step` of that job; `phase` < nq
 // for the query-block items that open a job's segment, == nq for K/V items.
 struct Cursor {
   int b, jb, step, phase;
@@ -181,12 +182,12 @@ struct Cursor {
   int left;                       // K/V steps left in this workgroup's range
 };
 
-template <typename T, int D, bool kSoftcap, bool kMulti>
+template <typename T, int D, bool kSoftcap, bool kMulti, bool kWide>
 __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeArgs a) {
-  using C = DecCfg<D>;
+  using C = DecCfg<D, kWide>;
   using L = typename C::L;
   __shared__ __attribute__((aligned(16))) char ring[C::NS * C::SB];
-  __shared__ __attribute__((aligned(16))) char mrg[4 * C::MSLOT];
+  __shared__ __attribute__((aligned(16))) char mrg[kWide ? 16 : 4 * C::MSLOT];  // (unused when wide)
   __shared__ int landed[C::NWP];       // items whose copies by producer p have landed
   __shared__ int consumed[C::NWC];     // items consumer wave w is done with
   __shared__ int mrg_written[4], mrg_read[4];  // merge handshakes per head block
@@ -196,10 +197,13 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave >= C::NWC;
   const int hb = wave & 3, par = (wave >> 2) & 1;  // consumer head block and step parity
+  // Consumer's 32-row block of the job: wide jobs give each consumer wave a
+  // block of its own and every K/V step, so the steps are read once for twice
+  // the rows; otherwise the two waves of a head block split the steps.
+  const int rb = kWide ? wave : hb;
   const int g = lane >> 5, c = lane & 31;
   const int G = a.Hq / a.Hkv;
   const int R = a.Sq * G;         // rows per kv head
-  const int jpb = a.Hkv * a.nhg;  // jobs per sequence
   const int P = gridDim.x;
   const int w_id = blockIdx.x;
 
@@ -216,18 +220,28 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   // 0 is loaded once and kept (a workgroup's range rarely goes past it).
   auto lens_chunk = [&](int c) -> int { return c * 64 + lane < a.B ? seq_len(a, c * 64 + lane) : 0; };
   const int len0 = lens_chunk(0);
+  // Jobs are listed head group first (all sequences' jobs of head group 0,
+  // then of group 1, ...), so with P a multiple of the group count the
+  // workgroups w, w + P/nhg, ... cover the same keys of the same sequence for
+  // the different query heads at the same time (one pass over the keys from
+  // memory, the others from cache).  Units of a sequence within one head
+  // group: Hkv jobs of (steps + SEG).
   auto units_of = [&](int L) -> long long {
     const int n = (L + C::BN - 1) / C::BN;
-    return n > 0 ? (long long)(n + C::SEG) * jpb : 0;
+    return n > 0 ? (long long)(n + C::SEG) * a.Hkv : 0;
   };
-  long long S = wave_sum64(units_of(len0));
-  for (int c = 1; c * 64 < a.B; ++c) S += wave_sum64(units_of(lens_chunk(c)));
-  S = uniform64(S);
+  long long S1 = wave_sum64(units_of(len0));
+  for (int c = 1; c * 64 < a.B; ++c) S1 += wave_sum64(units_of(lens_chunk(c)));
+  S1 = uniform64(S1);
+  const long long S = S1 * a.nhg;
   const int Pe = S < P ? (int)S : P;
   if (w_id >= Pe) return;  // the same for every wave of the workgroup
   const long long lo = (long long)w_id * S / Pe;
   const long long hi = (long long)(w_id + 1) * S / Pe;
-  // The sequence whose units contain lo, and the offset of lo inside them.
+  // The head group, the sequence whose units contain lo, and the offset of
+  // lo inside them.
+  const int hg0 = static_cast<int>(lo / S1);
+  const long long lo1 = lo - hg0 * S1;
   int b0 = 0;
   long long off0 = 0;
   {
@@ -235,14 +249,14 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     for (int c = 0; c * 64 < a.B; ++c) {
       const long long u = units_of(c == 0 ? len0 : lens_chunk(c));
       const long long incl = carry + wave_incl_scan64(u, lane);
-      const uint64_t hit = __ballot(u > 0 && incl - u <= lo && lo < incl);
+      const uint64_t hit = __ballot(u > 0 && incl - u <= lo1 && lo1 < incl);
       if (hit != 0) {
         const int src = __builtin_ctzll(hit);
         b0 = c * 64 + src;
         const long long excl = __shfl(incl, src, 64) - __shfl(u, src, 64);
         // (wave-uniform; readfirstlane tells the compiler so, keeping the
         // cursor in scalar registers)
-        off0 = __builtin_amdgcn_readfirstlane(static_cast<int>(lo - excl));
+        off0 = __builtin_amdgcn_readfirstlane(static_cast<int>(lo1 - excl));
         break;
       }
       carry = __shfl(incl, 63, 64);
@@ -278,12 +292,16 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     return __builtin_amdgcn_readfirstlane(b < 64 ? __shfl(len0, b, 64) : seq_len(a, b));
   };
   auto set_job = [&](Cursor& cu) {
-    cu.g_kv = cu.jb / a.nhg;
-    cu.hg = cu.jb - cu.g_kv * a.nhg;
+    cu.g_kv = cu.jb;
     cu.rows = min(C::ROWS, R - cu.hg * C::ROWS);
-    cu.nq = cu.rows > 64 ? 2 : 1;
+    cu.nq = (cu.rows + 63) / 64;
+  };
+  // Position of the cursor's job in the list (it orders the partial slots).
+  auto job_index = [&](const Cursor& cu) -> int64_t {
+    return ((int64_t)cu.hg * a.B + cu.b) * a.Hkv + cu.jb;
   };
   auto start = [&](Cursor& cu) {
+    cu.hg = hg0;
     cu.b = b0;
     cu.Lb = len_of(b0);
     cu.n = (cu.Lb + C::BN - 1) / C::BN;
@@ -316,10 +334,13 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     cu.left -= C::SEG;
     cu.step = 0;
     cu.phase = 0;
-    if (++cu.jb == jpb) {
+    if (++cu.jb == a.Hkv) {
       cu.jb = 0;
       do {
-        ++cu.b;
+        if (++cu.b == a.B) {  // on to the next head group's list
+          cu.b = 0;
+          ++cu.hg;
+        }
         cu.Lb = len_of(cu.b);
         cu.n = (cu.Lb + C::BN - 1) / C::BN;
       } while (cu.n == 0);
@@ -544,9 +565,32 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
   // natural-log LSE in fp32) to slot w + j.  Waves whose head block has no
   // query heads in this job still step the flags.
   auto finish_segment = [&](const Cursor& cc, bool job_end, int seg) {
-    const bool active = hb * 32 < cc.rows;
-    const int64_t j = (int64_t)cc.b * jpb + cc.jb;
+    const bool active = rb * 32 < cc.rows;
+    const int64_t j = job_index(cc);
     const int64_t slot = w_id + j;
+    if constexpr (kWide) {  // the wave holds its rows' whole state: write it
+      const bool poison = broken || __hip_atomic_load(&ring_broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (active) {
+        const float l_tot = pair_sum32(l_run);
+        const int row = rb * 32 + c;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint16_t* op = a.part_o + (slot * C::ROWS + row) * D;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint2 w2 = make_uint2(
+                f32_to_elem<T>(oacc[db][4 * rr] * inv) | (uint32_t)f32_to_elem<T>(oacc[db][4 * rr + 1] * inv) << 16,
+                f32_to_elem<T>(oacc[db][4 * rr + 2] * inv) | (uint32_t)f32_to_elem<T>(oacc[db][4 * rr + 3] * inv) << 16);
+            if (row < cc.rows) *reinterpret_cast<uint2*>(op + 32 * db + 8 * rr + 4 * g) = w2;
+          }
+        if (g == 0 && row < cc.rows)
+          a.part_lse[slot * C::ROWS + row] =
+              poison ? __builtin_nanf("") : (l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf);
+      }
+      if (lane == 0 && wave == 0 && job_end) a.job_seg[2 * j + 1] = w_id;  // this workgroup ends the job
+      return;
+    }
     char* ms = mrg + hb * C::MSLOT;
     uint2* ms_o = reinterpret_cast<uint2*>(ms);                       // [DBLK * 4][64] pairs of pairs
     float* ms_ml = reinterpret_cast<float*>(ms + 64 * 16 * C::DBLK * 2);  // m [64], l [64]
@@ -671,11 +715,11 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
     // The next group: a job's query items (read by every consumer wave), or
     // one K/V step per parity.
     const bool qgrp = cc.phase < cc.nq;
-    const int gsz = qgrp ? cc.nq : ((cc.left >= 2 && cc.step + 1 < cc.n) ? 2 : 1);
+    const int gsz = qgrp ? cc.nq : ((!kWide && cc.left >= 2 && cc.step + 1 < cc.n) ? 2 : 1);
     if (qgrp) {
       wait_landed(i + gsz);
-      if (lane == 0 && hb == 0 && par == 0 && cc.step == 0)  // this workgroup starts the job
-        a.job_seg[2 * ((int64_t)cc.b * jpb + cc.jb)] = w_id;
+      if (lane == 0 && wave == 0 && cc.step == 0)  // this workgroup starts the job
+        a.job_seg[2 * job_index(cc)] = w_id;
       m_run = kNegInf;
       l_run = 0.0f;
 #pragma unroll
@@ -683,12 +727,12 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
       if constexpr (kMulti) {
-        const int r0 = cc.hg * C::ROWS + hb * 32;
+        const int r0 = cc.hg * C::ROWS + rb * 32;
         lim_row = cc.Lb - a.Sq + 1 + min(r0 + c, R - 1) / G;
         lim_wave = cc.Lb - a.Sq + 1 + r0 / G;
       }
-      if (hb * 32 < cc.rows) {
-        const char* qt = ring + ((i + (hb >> 1)) % C::NS) * C::SB + (hb & 1) * C::TB;
+      if (rb * 32 < cc.rows) {
+        const char* qt = ring + ((i + (rb >> 1)) % C::NS) * C::SB + (rb & 1) * C::TB;
 #pragma unroll
         for (int ds = 0; ds < C::DSTEPS; ++ds) {
           uint4 raw = *reinterpret_cast<const uint4*>(qt + L::off(c, 2 * ds + g));
@@ -700,6 +744,14 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
         }
       }
       if (lane == 0) publish(&consumed[wave], i + gsz);
+    } else if constexpr (kWide) {  // one K/V step, read by every consumer wave
+      if (rb * 32 < cc.rows) {
+        wait_landed(i + 1);
+        kv_group(One{}, i, cc.step, cc.Lb);
+      }
+      if (lane == 0) publish(&consumed[wave], i + 1);
+      const bool job_end = cc.step + 1 == cc.n;
+      if (job_end || cc.left == 1) finish_segment(cc, job_end, seg++);
     } else {
       const bool mine = par < gsz && hb * 32 < cc.rows;
       // A parity-1 wave never reads item i of the group, so it is done with
@@ -723,16 +775,15 @@ __global__ __launch_bounds__(DecCfg<D>::NT, 1) void decode_split_kernel(DecodeAr
 // Merge the partial results of one job: one thread per (head row, 4 columns).
 // The job's partials are in slots w + j for w from its first to its last
 // workgroup, as recorded by the split kernel.
-template <typename T, int D>
+template <typename T, int D, int ROWS>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int TPH = D / 4;      // threads per head
   constexpr int HPB = 256 / TPH;  // heads per workgroup
-  constexpr int ROWS = DecCfg<D>::ROWS;
   constexpr int U = 8;            // partials loaded per round
   const int j = blockIdx.x;
-  const int jpb = a.Hkv * a.nhg;
-  const int b = j / jpb, jb = j % jpb;
-  const int g_kv = jb / a.nhg, hg = jb % a.nhg;
+  // job j of the split kernel's list: head group first, then sequence, kv head
+  const int hg = j / (a.B * a.Hkv);
+  const int b = (j / a.Hkv) % a.B, g_kv = j % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int rows = min(ROWS, a.Sq * G - hg * ROWS);
   const int r = blockIdx.y * HPB + threadIdx.x / TPH;
@@ -843,6 +894,26 @@ __global__ __launch_bounds__(256) void kvcache_append_kernel(DecodeArgs a) {
   *reinterpret_cast<uint4*>(vd) = *reinterpret_cast<const uint4*>(vs);
 }
 
+template <typename T, int D, bool W>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
+  const dim3 block(DecCfg<D, W>::NT);
+  const bool multi = a.causal && a.Sq > 1;
+  if (a.softcap > 0.0f) {
+    if (multi) hipLaunchKernelGGL((decode_split_kernel<T, D, true, true, W>), dim3(a.parts), block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, true, false, W>), dim3(a.parts), block, 0, s, a);
+  } else {
+    if (multi) hipLaunchKernelGGL((decode_split_kernel<T, D, false, true, W>), dim3(a.parts), block, 0, s, a);
+    else hipLaunchKernelGGL((decode_split_kernel<T, D, false, false, W>), dim3(a.parts), block, 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int ROWS = DecCfg<D, W>::ROWS;
+  constexpr int HPB = 256 / (D / 4);
+  const int jobs = a.B * a.Hkv * a.nhg;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, ROWS>), dim3(jobs, (ROWS + HPB - 1) / HPB), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   if (a.len_add > 0) {
@@ -851,28 +922,22 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 block(DecCfg<D>::NT);
-  const bool multi = a.causal && a.Sq > 1;
-  if (a.softcap > 0.0f) {
-    if (multi) hipLaunchKernelGGL((decode_split_kernel<T, D, true, true>), dim3(a.parts), block, 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<T, D, true, false>), dim3(a.parts), block, 0, s, a);
-  } else {
-    if (multi) hipLaunchKernelGGL((decode_split_kernel<T, D, false, true>), dim3(a.parts), block, 0, s, a);
-    else hipLaunchKernelGGL((decode_split_kernel<T, D, false, false>), dim3(a.parts), block, 0, s, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  constexpr int HPB = 256 / (D / 4);
-  const int jobs = a.B * a.Hkv * a.nhg;
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(jobs, (DecCfg<D>::ROWS + HPB - 1) / HPB), dim3(256),
-                     0, s, a);
-  return hipGetLastError();
+  if (a.rows_job == kDecodeRowsWide) return launch_split<T, D, true>(a, s);
+  if (a.rows_job == kDecodeRows) return launch_split<T, D, false>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+// A kv head with more than 128 rows takes 256-row jobs: its keys are then
+// streamed once per 256 rows instead of once per 128.
+int decode_job_rows(int Hq, int Hkv, int Sq) {
+  return (int64_t)Sq * (Hq / Hkv) > kDecodeRows ? kDecodeRowsWide : kDecodeRows;
+}
+
 int decode_head_groups(int Hq, int Hkv, int Sq) {
-  return (int)(((int64_t)Sq * (Hq / Hkv) + kDecodeRows - 1) / kDecodeRows);
+  const int rows = decode_job_rows(Hq, Hkv, Sq);
+  return (int)(((int64_t)Sq * (Hq / Hkv) + rows - 1) / rows);
 }
 
 int device_cu_count() {
@@ -894,10 +959,11 @@ DecodeWorkspace decode_workspace(int B, int Hq, int Hkv, int Sq, int D, int part
   DecodeWorkspace w;
   const size_t jobs = (size_t)B * Hkv * decode_head_groups(Hq, Hkv, Sq);
   const size_t slots = (size_t)parts + jobs;
+  const size_t rows = decode_job_rows(Hq, Hkv, Sq);
   w.status_off = 0;  // the status word; 256 bytes keep the rest aligned
   w.o_off = 256;
-  w.lse_off = w.o_off + (slots * kDecodeRows * D * sizeof(uint16_t) + 255) / 256 * 256;
-  w.seg_off = w.lse_off + (slots * kDecodeRows * sizeof(float) + 255) / 256 * 256;
+  w.lse_off = w.o_off + (slots * rows * D * sizeof(uint16_t) + 255) / 256 * 256;
+  w.seg_off = w.lse_off + (slots * rows * sizeof(float) + 255) / 256 * 256;
   w.bytes = w.seg_off + (jobs * 2 * sizeof(int32_t) + 255) / 256 * 256;
   return w;
 }

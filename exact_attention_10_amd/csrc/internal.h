@@ -128,11 +128,12 @@ struct DecodeArgs {
   float scale;
   float softcap;
   int parts;                 // workgroups; the key work is cut into this many equal ranges
-  int nhg;                   // groups of up to kDecodeRows query heads per kv head
-  uint16_t* part_o;          // workspace [parts + jobs][kDecodeRows][D]: normalised partial O,
+  int rows_job;              // rows per job: decode_job_rows()
+  int nhg;                   // groups of up to rows_job rows per kv head
+  uint16_t* part_o;          // workspace [parts + jobs][rows_job][D]: normalised partial O,
                              // rounded to the input type
-  float* part_lse;           // workspace [parts + jobs][kDecodeRows]
-                             // (a job: sequence, kv head, up to kDecodeRows rows)
+  float* part_lse;           // workspace [parts + jobs][rows_job]
+                             // (a job: sequence, kv head, up to rows_job rows)
   int32_t* job_seg;          // workspace [jobs][2]: first and last workgroup of each job
   // KV-cache addressing.  Contiguous: sequence b uses batch row batch_idx[b]
   // (b when null) of k/v.  Paged (block_table != null): row r of sequence b is
@@ -153,7 +154,9 @@ struct DecodeArgs {
 // Bits of the decode status word.
 constexpr uint32_t kDecodeStatusLength = 1;  // a cache length was outside [0, Smax - s_new]
 constexpr uint32_t kDecodeStatusWait = 2;    // an in-kernel wait expired (rows poisoned with NaN)
-constexpr int kDecodeRows = 128;  // rows (query, head) per decode job
+constexpr int kDecodeRows = 128;      // rows (query, head) per decode job
+constexpr int kDecodeRowsWide = 256;  // the same when a kv head has more than 128 rows
+int decode_job_rows(int Hq, int Hkv, int Sq);
 // Number of workgroups: num_splits when > 0, else the device's compute units.
 int decode_parts(int num_splits);
 int device_cu_count();  // compute units of the current device (cached per device)

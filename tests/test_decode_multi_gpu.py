@@ -49,10 +49,13 @@ def f64(x):
 CFGS = [
     # B, Sq, Hq, Hkv, D, Smax, lens, causal, softcap
     (4, 4, 32, 8, 128, 512, [512, 2, 100, 33], True, 0.0),      # 16 rows per kv head: one job
-    (3, 3, 128, 1, 128, 1024, [1024, 700, 3], True, 4.0),       # 384 rows: three jobs per sequence
+    (3, 3, 128, 1, 128, 1024, [1024, 700, 3], True, 4.0),       # 384 rows: 256- and 128-row jobs
     (2, 5, 16, 2, 64, 256, [256, 77], False, 0.0),              # non-causal: every row sees all keys
     (2, 2, 40, 1, 64, 256, [1, 200], True, 0.0),                # rows mix positions inside a job
     (2, 64, 8, 8, 128, 300, [300, 64], True, 0.0),              # a 64-query chunk
+    (2, 4, 64, 1, 64, 256, [256, 130], True, 0.0),              # 256 rows: one wide job, D 64
+    (3, 3, 64, 1, 128, 512, [512, 40, 3], False, 0.0),          # 192 rows: a wide job, two blocks idle
+    (2, 8, 64, 2, 128, 640, [640, 300], True, 0.0),             # 512 rows per kv head: two wide jobs
 ]
 
 
