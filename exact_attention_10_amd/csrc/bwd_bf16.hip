@@ -884,6 +884,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
   // 1 and 2 (with a document mask) one 64-entry row of lse2, Delta and the
   // rows' document ids.  Rows past Sq repeat the last row (masked by wave A,
   // and their P' is zero for wave B).
+  // (Copies stay compiler-visible here: issued from inline assembly, which
+  // lets the compiler count LDS reads precisely, this kernel was 19% slower.)
   const TileCopy<D, C::NW> qcopy(qp, a.q_ss, a.Sq, wave, lane);
   const TileCopy<D, C::NW> dcopy(dop, a.do_ss, a.Sq, wave, lane);
   auto load_tile = [&](int t, auto buf_tag) __attribute__((always_inline)) {
@@ -1254,16 +1256,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int fold) {
 
   // K and V of tile kt into buffer BUF, and (document masks) the tile's 64
   // key document ids, copied by wave 0; every wait below is a full one.
-  const TileCopy<D> kcopy(kp, a.k_ss, a.Sk, wave, lane);
-  const TileCopy<D> vcopy(vp, a.v_ss, a.Sk, wave, lane);
+  // Copies issued from inline assembly (dma16 / dma4): copies the compiler
+  // can see make it treat every LDS read as unordered and wait for each one
+  // in full (lgkmcnt(0)); hidden from it, the fragment reads overlap.
+  const TileCopy<D, 4, true> kcopy(kp, a.k_ss, a.Sk, wave, lane);
+  const TileCopy<D, 4, true> vcopy(vp, a.v_ss, a.Sk, wave, lane);
   auto load_tile = [&](int kt, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     kcopy(reinterpret_cast<bf16_t*>(BUF ? lk1 : lk0), kt * C::BN);
     vcopy(reinterpret_cast<bf16_t*>(BUF ? lv1 : lv0), kt * C::BN);
     if (has_doc && wave == 0) {
       const int j = min(kt * C::BN + lane, a.Sk - 1);  // keys past Sk are masked
-      __builtin_amdgcn_global_load_lds(dock + j, (__attribute__((address_space(3))) void*)(BUF ? lz1 : lz0),
-                                       4, 0, 0);
+      dma4(dock + j, lds_addr(BUF ? lz1 : lz0));
     }
   };
   using B0 = std::integral_constant<int, 0>;

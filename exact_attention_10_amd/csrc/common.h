@@ -147,62 +147,6 @@ struct TileLayout {
   }
 };
 
-// Wave-cooperative copy of rows [row0, row0 + 64) of a [rows, D] bf16 matrix
-// (row stride `ld` elements) into a TileLayout image at `tile`.  Rows at or
-// past `nrows` are read from row nrows - 1 instead (callers mask them), so no
-// address leaves the matrix.  NW waves; wave w copies groups w, w + NW, ...
-template <int D, int NW = 4>
-__device__ __forceinline__ void tile_dma(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
-                                         int nrows, int wave, int lane) {
-  using L = TileLayout<D>;
-  static_assert((64 / L::RG) % NW == 0, "groups must divide among the waves");
-#pragma unroll
-  for (int u = 0; u < 64 / L::RG / NW; ++u) {
-    const int grp = wave + NW * u;
-    const int row = grp * L::RG + lane % L::RG;
-    const int chunk = lane / L::RG;
-    int key = row0 + row;
-    key = key < nrows ? key : nrows - 1;
-    const bf16_t* gp = src + (int64_t)key * ld + chunk * 8;
-    bf16_t* lp = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(tile) + grp * L::GS);
-    __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
-  }
-}
-
-// The same copy with the per-lane part of the address computed once: a tile
-// at row0 then costs one scalar base and one 64-bit add per copy (the
-// clamping form above is kept for a tile that runs past nrows).
-template <int D, int NW = 4>
-struct TileCopy {
-  using L = TileLayout<D>;
-  static constexpr int NU = 64 / L::RG / NW;  // copies per lane per tile
-  static_assert((64 / L::RG) % NW == 0, "groups must divide among the waves");
-  const bf16_t* src;
-  int64_t ld;
-  int64_t lane_off;  // bytes from a tile's first row to this lane's 16 bytes (copy 0)
-  int nrows, wave, lane;
-  __device__ TileCopy(const bf16_t* src_, int64_t ld_, int nrows_, int wave_, int lane_)
-      : src(src_), ld(ld_), nrows(nrows_), wave(wave_), lane(lane_) {
-    lane_off = ((int64_t)(wave_ * L::RG + lane_ % L::RG) * ld_ + (lane_ / L::RG) * 8) * 2;
-  }
-  // elem_off: elements added to the source (another head of the same layout)
-  __device__ __forceinline__ void operator()(bf16_t* tile, int row0, int64_t elem_off = 0) const {
-    if (row0 + 64 > nrows) {
-      tile_dma<D, NW>(tile, src + elem_off, ld, row0, nrows, wave, lane);
-      return;
-    }
-    const char* base = reinterpret_cast<const char*>(src + elem_off) + (int64_t)row0 * ld * 2;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const char* gp = base + (int64_t)u * NW * L::RG * ld * 2 + lane_off;
-      char* lp = reinterpret_cast<char*>(tile) + (wave + NW * u) * L::GS;
-      __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
-    }
-  }
-};
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -221,7 +165,81 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_base), "v"(gptr) : "memory", "m0");
 }
+// The same with 4 bytes per lane (global_load_lds_dword): lane i's word lands
+// at lds_base + 4 * i.
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_base), "v"(gptr) : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Wave-cooperative copy of rows [row0, row0 + 64) of a [rows, D] bf16 matrix
+// (row stride `ld` elements) into a TileLayout image at `tile`.  Rows at or
+// past `nrows` are read from row nrows - 1 instead (callers mask them), so no
+// address leaves the matrix.  NW waves; wave w copies groups w, w + NW, ...
+// ASM: issue the copies from inline assembly (dma16), so the compiler's wait
+// counting never sees them (the caller waits with wait_dma()).
+template <int D, int NW = 4, bool ASM = false>
+__device__ __forceinline__ void tile_dma(bf16_t* tile, const bf16_t* src, int64_t ld, int row0,
+                                         int nrows, int wave, int lane) {
+  using L = TileLayout<D>;
+  static_assert((64 / L::RG) % NW == 0, "groups must divide among the waves");
+#pragma unroll
+  for (int u = 0; u < 64 / L::RG / NW; ++u) {
+    const int grp = wave + NW * u;
+    const int row = grp * L::RG + lane % L::RG;
+    const int chunk = lane / L::RG;
+    int key = row0 + row;
+    key = key < nrows ? key : nrows - 1;
+    const bf16_t* gp = src + (int64_t)key * ld + chunk * 8;
+    bf16_t* lp = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(tile) + grp * L::GS);
+    if constexpr (ASM)
+      dma16(gp, lds_addr(lp));
+    else
+      __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+  }
+}
+
+// The same copy with the per-lane part of the address computed once: a tile
+// at row0 then costs one scalar base and one 64-bit add per copy (the
+// clamping form above is kept for a tile that runs past nrows).  ASM as in
+// tile_dma.
+template <int D, int NW = 4, bool ASM = false>
+struct TileCopy {
+  using L = TileLayout<D>;
+  static constexpr int NU = 64 / L::RG / NW;  // copies per lane per tile
+  static_assert((64 / L::RG) % NW == 0, "groups must divide among the waves");
+  const bf16_t* src;
+  int64_t ld;
+  int64_t lane_off;  // bytes from a tile's first row to this lane's 16 bytes (copy 0)
+  int nrows, wave, lane;
+  __device__ TileCopy(const bf16_t* src_, int64_t ld_, int nrows_, int wave_, int lane_)
+      : src(src_), ld(ld_), nrows(nrows_), wave(wave_), lane(lane_) {
+    lane_off = ((int64_t)(wave_ * L::RG + lane_ % L::RG) * ld_ + (lane_ / L::RG) * 8) * 2;
+  }
+  // elem_off: elements added to the source (another head of the same layout)
+  __device__ __forceinline__ void operator()(bf16_t* tile, int row0, int64_t elem_off = 0) const {
+    if (row0 + 64 > nrows) {
+      tile_dma<D, NW, ASM>(tile, src + elem_off, ld, row0, nrows, wave, lane);
+      return;
+    }
+    const char* base = reinterpret_cast<const char*>(src + elem_off) + (int64_t)row0 * ld * 2;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const char* gp = base + (int64_t)u * NW * L::RG * ld * 2 + lane_off;
+      char* lp = reinterpret_cast<char*>(tile) + (wave + NW * u) * L::GS;
+      if constexpr (ASM)
+        dma16(gp, lds_addr(lp));
+      else
+        __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+
 
 // Per-row allowed key interval for causal / sliding-window masks.
 // With delta = Sk - Sq, row i may attend keys j with

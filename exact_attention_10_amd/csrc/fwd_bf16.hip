@@ -82,7 +82,9 @@ __device__ __forceinline__ constexpr int koff(int kb, int r) { return 32 * kb + 
 
 // One 64-key tile: S^T = K Q^T, online softmax update, O^T += V^T P^T.
 // MASKED evaluates the mask predicate per element (partial tiles only).
-template <typename T, int D, int MOD, bool MASKED>
+// LEAN: the kernel runs at the 168-register budget (three workgroups per
+// CU), so fewer LDS fragments are read ahead.
+template <typename T, int D, int MOD, bool MASKED, bool LEAN>
 __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_base,
                                          const int* doc_t, const typename T::vec8 (&qf)[D / 16],
                                          f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
@@ -93,26 +95,58 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
   constexpr bool kScaled = kAlibi || kSoftcap;
   const int g = lane >> 5, c = lane & 31;
 
-  // S^T for the two 32-key halves.  The two accumulators are updated in
-  // alternation so consecutive MFMAs never depend on each other (a dependent
-  // accumulation waits for the previous MFMA to drain).
+  // S^T for the two 32-key halves.  MFMA i (i = 2*ds + kb) takes K fragment
+  // (key half kb, d-step ds); the two accumulators alternate so consecutive
+  // MFMAs never depend on each other.  The K fragments are read from LDS
+  // kSPF MFMAs ahead: the scheduling groups below fix the order "kSPF reads,
+  // then (one MFMA, one read) pairs, then the last MFMAs", so each MFMA waits
+  // only for a read issued kSPF MFMAs earlier instead of one round trip per
+  // MFMA.
+  constexpr int kNS = 2 * C::DSTEPS;            // S MFMAs per tile
+  constexpr int kSPF = kNS < 8 ? kNS : 8;       // K reads in flight
   f32x16 sacc[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+  typename T::vec8 kf[kNS];
 #pragma unroll
-  for (int ds = 0; ds < C::DSTEPS; ds += 2) {
-    typename T::vec8 ka[2][2];
+  for (int i = 0; i < kNS; ++i)
+    kf[i] = *reinterpret_cast<const typename T::vec8*>(kb_base + C::L::off(32 * (i & 1) + c, 2 * (i >> 1) + g));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < kNS; ++i) sacc[i & 1] = mfma32(kf[i], qf[i >> 1], sacc[i & 1]);
+
+  // V^T fragments of the first PV steps are read now, behind the K reads:
+  // they do not depend on the softmax, so they land while it runs.
+  // Fragment f = kk * DBLK + db: keys 16*kk.., output block db.
+  constexpr int kNV = 4 * C::DBLK;              // PV MFMAs per tile
+  constexpr int kVPF = LEAN ? 0 : C::DBLK;      // V fragments read ahead
+  const int beta = lane >> 4, s16 = lane & 15;
+  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
+  const int tr_chunk = 2 * (beta & 1) + ((s16 & 3) >> 1);
+  const int tr_half = 8 * (s16 & 1);
+  auto vfrag = [&](int f) __attribute__((always_inline)) {
+    const int kk = f / C::DBLK, db = f % C::DBLK;
+    const char* p0 = vb_base + C::L::off(16 * kk + tr_row, 4 * db + tr_chunk) + tr_half;
+    const char* p1 = vb_base + C::L::off(16 * kk + 8 + tr_row, 4 * db + tr_chunk) + tr_half;
+    return cat_frag<typename T::vec8>(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
+                                      lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
+  };
+  typename T::vec8 vf[kNV];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        ka[kb][u] = *reinterpret_cast<const typename T::vec8*>(kb_base + C::L::off(32 * kb + c, 2 * (ds + u) + g));
+  for (int f = 0; f < kVPF; ++f) vf[f] = vfrag(f);
+
+  // (At the 168-register budget the compiler's own order is kept: reads
+  // ahead cost registers there, and spills cost more than the waits.)
+  if constexpr (!LEAN) {
+    __builtin_amdgcn_sched_group_barrier(0x100, kSPF, 0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[kb][u], qf[ds + u], sacc[kb]);
+    for (int i = 0; i < kNS - kSPF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kSPF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVPF, 0);
   }
 
   // Scores in the exp2 domain (raw dot products when no modifier: the
@@ -211,25 +245,24 @@ __device__ __forceinline__ void fwd_tile(const char* kb_base, const char* vb_bas
     }
   l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-  // O^T += V^T P^T; V^T fragments by transposed LDS reads.  For each
-  // 16-key step the D/32 output blocks are independent accumulators, issued
-  // back to back.
-  const int beta = lane >> 4, s16 = lane & 15;
-  const int tr_row = 4 * (beta >> 1) + (s16 >> 2);
-  const int tr_chunk = 2 * (beta & 1) + ((s16 & 3) >> 1);
-  const int tr_half = 8 * (s16 & 1);
+  // O^T += V^T P^T; V^T fragments by transposed LDS reads, kVPF fragments
+  // ahead of their MFMA (the first kVPF were read before the softmax).  For
+  // each 16-key step the D/32 output blocks are independent accumulators,
+  // issued back to back.
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    typename T::vec8 va[C::DBLK];
+  for (int f = kVPF; f < kNV; ++f) vf[f] = vfrag(f);
 #pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) {
-      const char* p0 = vb_base + C::L::off(16 * kk + tr_row, 4 * db + tr_chunk) + tr_half;
-      const char* p1 = vb_base + C::L::off(16 * kk + 8 + tr_row, 4 * db + tr_chunk) + tr_half;
-      va[db] = cat_frag<typename T::vec8>(lds_read_tr16(reinterpret_cast<const bf16_t*>(p0)),
-                        lds_read_tr16(reinterpret_cast<const bf16_t*>(p1)));
+  for (int f = 0; f < kNV; ++f) {
+    const int kk = f / C::DBLK, db = f % C::DBLK;
+    oacc[db] = mfma32(vf[f], pf[kk >> 1][kk & 1], oacc[db]);
+  }
+  if constexpr (!LEAN) {
+#pragma unroll
+    for (int f = 0; f < kNV - kVPF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) oacc[db] = mfma32(va[db], pf[kk >> 1][kk & 1], oacc[db]);
+    __builtin_amdgcn_sched_group_barrier(0x008, kVPF, 1);
   }
 }
 
@@ -371,8 +404,14 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
   const int delta = a.Sk - a.Sq;
 
   int doc_r = 0;
-  const TileCopy<D, C::WPG> kcopy(kp, a.k_ss, a.Sk, wave, lane);
-  const TileCopy<D, C::WPG> vcopy(vp, a.v_ss, a.Sk, wave, lane);
+  // Copies issued from inline assembly: with the builtin, the compiler counts
+  // the pending copies as LDS traffic of unknown order and waits for every
+  // LDS read in full (lgkmcnt(0)), which serialises the fragment reads.
+  // (Not at the 168-register budget, where the copies' 64-bit addresses,
+  // which the builtin folds into its offset field, cost registers.)
+  constexpr bool kAsmCopy = C::MINB < 3;
+  const TileCopy<D, C::WPG, kAsmCopy> kcopy(kp, a.k_ss, a.Sk, wave, lane);
+  const TileCopy<D, C::WPG, kAsmCopy> vcopy(vp, a.v_ss, a.Sk, wave, lane);
   // K and V of tile kt into buffer BUF (direct global->LDS), and this
   // thread's document id of the tile into a register.
   auto load_tile = [&](int kt, auto buf_tag) {
@@ -473,7 +512,7 @@ __global__ __launch_bounds__(64 * NW, (FwdCfg<D, NW, NG>::MINB)) void fwd_bf16_k
         if (!sparse) trace_row[cur.kt] = cur.full ? 2 : 1;
         else if (cur.kt % a.tiles.sub == 0) trace_row[cur.kt / a.tiles.sub] = cur.full ? 2 : 1;
       }
-      fwd_tile<T, D, MOD, decltype(masked)::value>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
+      fwd_tile<T, D, MOD, decltype(masked)::value, C::MINB >= 3>(BUF ? lds_k1 : lds_k0, BUF ? lds_v1 : lds_v0,
                                                 BUF ? lds_doc1 : lds_doc0, qf, oacc, m_run, l_run,
                                                 ctx, cur.kt * C::BN, lane);
     }
