@@ -248,14 +248,14 @@ __device__ __forceinline__ void dkdv_scores(const char* qt_lds, const char* dot_
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        int4 d4 = make_int4(0, 0, 0, 0);
-        if (has_doc) d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
+        // (document ids read whatever has_doc says, and ignored without a
+        // document mask: a test guarded by has_doc became a branch per element)
+        const int4 d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
         const int dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rr + e;
-          bool ok = static_cast<uint32_t>(ib + roff(qb, r)) < span;
-          if (has_doc) ok = ok && dv4[e] == my_doc;
+          const bool ok = (static_cast<uint32_t>(ib + roff(qb, r)) < span) & (!has_doc | (dv4[e] == my_doc));
           s[qb][r] = ok ? s[qb][r] : 0.0f;
           dp[qb][r] = ok ? dp[qb][r] : 0.0f;
         }
@@ -667,8 +667,11 @@ __device__ __forceinline__ void pair_side_a(const char* qt_lds, const char* dot_
     for (int rr = 0; rr < 4; ++rr) {
       const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qb + 8 * rr + 4 * g);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      // (on partial tiles the document ids are read whatever has_doc says and
+      // ignored without a document mask: a test guarded by has_doc became a
+      // branch per element)
       int dv4[4] = {0, 0, 0, 0};
-      if (masked && has_doc) {
+      if (masked) {
         const int4 d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
         dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
       }
@@ -681,8 +684,7 @@ __device__ __forceinline__ void pair_side_a(const char* qt_lds, const char* dot_
         if (masked) {
           // rows [rows_first, rows_first + rows_count) may see this key; with
           // a document mask the row's document must also be the key's
-          bool ok = static_cast<uint32_t>(ib + roff(qb, r)) < span;
-          if (has_doc) ok = ok && dv4[e] == my_doc;
+          const bool ok = (static_cast<uint32_t>(ib + roff(qb, r)) < span) & (!has_doc | (dv4[e] == my_doc));
           p = ok ? p : 0.0f;
         }
         pf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(p);
@@ -1114,8 +1116,11 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
+      // (on partial tiles the document ids are read whatever has_doc says and
+      // ignored without a document mask: a test guarded by has_doc became a
+      // branch per element)
       int4 d4 = make_int4(0, 0, 0, 0);
-      if (MASKED && has_doc) d4 = *reinterpret_cast<const int4*>(dock_t + 32 * kb + 8 * rr + 4 * g);
+      if (MASKED) d4 = *reinterpret_cast<const int4*>(dock_t + 32 * kb + 8 * rr + 4 * g);
       const int dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1124,8 +1129,7 @@ __device__ __forceinline__ void dq_tile(const char* kt_lds, const char* vt_lds, 
         const int j = key_base + 4 * g + roff(kb, r);
         float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[kb][r], lse2, cx, my_q + cx.delta_pos - j, &th));
         if (MASKED) {
-          bool ok = static_cast<uint32_t>(jb + roff(kb, r)) < span;
-          if (has_doc) ok = ok && dv4[e] == my_doc;
+          const bool ok = (static_cast<uint32_t>(jb + roff(kb, r)) < span) & (!has_doc | (dv4[e] == my_doc));
           p = ok ? p : 0.0f;
         }
         float dsv = p * (dp[kb][r] - dl);
