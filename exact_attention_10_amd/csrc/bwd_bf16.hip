@@ -539,29 +539,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a, int partial
   if (t < ntiles) step(t++, B0{});
   if (t < ntiles) step(t++, B1{});
 
-  // dv[db][r], dk[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c.
+  // dv[db][r], dk[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c.  One
+  // base address per lane and output, per-element offsets in multiples of the
+  // key stride, the key bound tested only when the wave's keys run past Sk.
   const float scale = a.scale;
-#pragma unroll
-  for (int db = 0; db < C::DBLK; ++db) {
+  const int key0 = kv0 + 4 * g;
+  const bool whole = kv0 + 32 <= a.Sk;
+  auto stores = [&](auto kout, auto vout, int64_t kst, int64_t vst, auto conv) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key >= a.Sk) continue;
-      const int d = 32 * db + c;
-      const float vval = dv[db][r];
-      const float kval = dk[db][r] * scale;
-      if (partial) {
-        // fp32 partials [B, Sk, Hq, D] in the workspace, summed per group later.
-        const int64_t idx = (((int64_t)b * a.Sk + key) * a.Hq + h) * D + d;
-        a.part_dk[idx] = kval;
-        a.part_dv[idx] = vval;
-      } else {
-        bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)key * a.dk_ss + kvh * a.dk_sh;
-        bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)key * a.dv_ss + kvh * a.dv_sh;
-        dkp[d] = f32_to_elem<T>(kval);
-        dvp[d] = f32_to_elem<T>(vval);
+      const int ko = 8 * (r >> 2) + (r & 3);
+      if (!whole && key0 + ko >= a.Sk) continue;
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) {
+        kout[ko * kst + 32 * db] = conv(dk[db][r] * scale);
+        vout[ko * vst + 32 * db] = conv(dv[db][r]);
       }
     }
+  };
+  if (partial) {
+    // fp32 partials [B, Sk, Hq, D] in the workspace, summed per group later.
+    const int64_t i0 = (((int64_t)b * a.Sk + key0) * a.Hq + h) * D + c;
+    stores(a.part_dk + i0, a.part_dv + i0, (int64_t)a.Hq * D, (int64_t)a.Hq * D, [](float v) { return v; });
+  } else {
+    bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)key0 * a.dk_ss + kvh * a.dk_sh + c;
+    bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)key0 * a.dv_ss + kvh * a.dv_sh + c;
+    stores(dkp, dvp, a.dk_ss, a.dv_ss, [](float v) { return f32_to_elem<T>(v); });
   }
 }
 
@@ -971,26 +974,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_kernel(BwdArgs a, int pa
 
   // acc[db][r]: key kv0 + 8*(r/4) + 4*g + r%4, d = 32*db + c; wave A holds
   // dV, wave B dK (scaled here).
+  // One base address per lane (its first key and d = c) and per-element
+  // offsets that are multiples of the key stride; the key bound is tested only
+  // when the wave's 32 keys run past Sk.
   const float mul = side_a ? 1.0f : a.scale;
-#pragma unroll
-  for (int db = 0; db < C::DBLK; ++db) {
+  const int key0 = kv0 + 4 * g;
+  const bool whole = kv0 + 32 <= a.Sk;
+  auto stores = [&](auto out, int64_t kstride, auto conv) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key >= a.Sk) continue;
-      const int d = 32 * db + c;
-      const float val = acc[db][r] * mul;
-      if (partial) {
-        const int64_t idx = (((int64_t)b * a.Sk + key) * a.Hq + h) * D + d;
-        (side_a ? a.part_dv : a.part_dk)[idx] = val;
-      } else if (side_a) {
-        bf16_t* dvp = static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)key * a.dv_ss + kvh * a.dv_sh;
-        dvp[d] = f32_to_elem<T>(val);
-      } else {
-        bf16_t* dkp = static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)key * a.dk_ss + kvh * a.dk_sh;
-        dkp[d] = f32_to_elem<T>(val);
-      }
+      const int ko = 8 * (r >> 2) + (r & 3);
+      if (!whole && key0 + ko >= a.Sk) continue;
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) out[ko * kstride + 32 * db] = conv(acc[db][r] * mul);
     }
+  };
+  if (partial) {
+    float* base = (side_a ? a.part_dv : a.part_dk) + (((int64_t)b * a.Sk + key0) * a.Hq + h) * D + c;
+    stores(base, (int64_t)a.Hq * D, [](float v) { return v; });
+  } else {
+    bf16_t* base = side_a ? static_cast<bf16_t*>(a.dv) + b * a.dv_sb + (int64_t)key0 * a.dv_ss + kvh * a.dv_sh + c
+                          : static_cast<bf16_t*>(a.dk) + b * a.dk_sb + (int64_t)key0 * a.dk_ss + kvh * a.dk_sh + c;
+    stores(base, side_a ? a.dv_ss : a.dk_ss, [](float v) { return f32_to_elem<T>(v); });
   }
 }
 
