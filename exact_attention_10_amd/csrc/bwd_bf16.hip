@@ -664,36 +664,46 @@ __device__ __forceinline__ void pair_side_a(const char* qt_lds, const char* dot_
   f16x8 xh[2][2];  // P' for wave B, in fp16 whatever the input type (P' lies in [0, 1])
   const uint32_t span = static_cast<uint32_t>(rows_count);
   const int ib = q0 + 4 * g - rows_first;
+  // P for every element, with the predicate compiled only into the partial
+  // tiles' copy (kept inside the loop as a runtime test, the compiler turned
+  // it into selects that every tile paid for).  Only P is written in the two
+  // branches; the accumulators are not touched before they join.
+  auto probs = [&](auto mtag) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(mtag)::value;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qb + 8 * rr + 4 * g);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      // (on partial tiles the document ids are read whatever has_doc says and
-      // ignored without a document mask: a test guarded by has_doc became a
-      // branch per element)
-      int dv4[4] = {0, 0, 0, 0};
-      if (masked) {
-        const int4 d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
-        dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rr + e;
-        float th = 0.0f;
-        const int i = q0 + roff(qb, r) + 4 * g;
-        float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[qb][r], lv[e], cx, i + cx.delta_pos - my_key, &th));
-        if (masked) {
-          // rows [rows_first, rows_first + rows_count) may see this key; with
-          // a document mask the row's document must also be the key's
-          const bool ok = (static_cast<uint32_t>(ib + roff(qb, r)) < span) & (!has_doc | (dv4[e] == my_doc));
-          p = ok ? p : 0.0f;
+      for (int rr = 0; rr < 4; ++rr) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_t + 32 * qb + 8 * rr + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        // (the document ids are read whatever has_doc says and ignored without
+        // a document mask: a test guarded by has_doc became a branch per element)
+        int dv4[4] = {0, 0, 0, 0};
+        if constexpr (kMasked) {
+          const int4 d4 = *reinterpret_cast<const int4*>(docq_t + 32 * qb + 8 * rr + 4 * g);
+          dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
         }
-        pf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(p);
-        xh[qb][r >> 3][r & 7] = static_cast<_Float16>(kSoftcap ? p * (1.0f - th * th) : p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rr + e;
+          float th = 0.0f;
+          const int i = q0 + roff(qb, r) + 4 * g;
+          float p = fast_exp2(score_minus<kAlibi, kSoftcap>(s[qb][r], lv[e], cx, i + cx.delta_pos - my_key, &th));
+          if constexpr (kMasked) {
+            // rows [rows_first, rows_first + rows_count) may see this key; with
+            // a document mask the row's document must also be the key's
+            const bool ok = (static_cast<uint32_t>(ib + roff(qb, r)) < span) & (!has_doc | (dv4[e] == my_doc));
+            p = ok ? p : 0.0f;
+          }
+          pf[qb][r >> 3][r & 7] = static_cast<typename T::elem>(p);
+          xh[qb][r >> 3][r & 7] = static_cast<_Float16>(kSoftcap ? p * (1.0f - th * th) : p);
+        }
       }
-    }
+  };
+  if (masked)
+    probs(std::true_type{});
+  else
+    probs(std::false_type{});
   // hand-over: chunk j = 2 qb + h of every lane at j * 1 KB + 16 * lane
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
